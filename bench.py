@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the k-quant decode matvec on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Default workload (one "step"): the 52-layer decode stream -- 52 independent
+Q/K/V/gate sets (hidden 6,656 -> 4096/256/256/4096; Q and gate Q4_K on even
+layers and Q5_K on odd layers, K and V Q6_K), one grid-split kq_matvec_set
+launch per layer, each layer with its own weights and its own x, ntok = 1,
+1,917,460,480 weight bytes per step.  Weights and activations are seeded
+synthetic data (kqgen) resident in HBM before the timed region.
+
+Prints ONE JSON line: effective weight GB/s over the whole step (launch gaps
+included), the roofline of the set kernel (bytes per launch / the average
+launch duration from HIP events recorded on the launch stream), and the CPU
+oracle's rate on a bounded sample on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="stream52",
+                   choices=["stream52", "qkvg_set", "lm_head", "single_q4k", "kv_pair"])
+    p.add_argument("--ntok", type=int, default=1, help="kv_pair only")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def build_workload(name, ntok):
+    from kqgen import workloads as wl
+    if name == "stream52":
+        return wl.qkvg_stream(), "qkvg_stream_52_layers", 1
+    if name == "qkvg_set":
+        # one layer's set, rotated over 16 distinct seeded copies so that the
+        # weights come from HBM rather than the 256 MB last-level cache
+        return [wl.qkvg_layer(2, i) for i in range(16)], "qkvg_set_x16_rotating", 1
+    if name == "lm_head":
+        return wl.lm_head(), "lm_head_q6k_202048x6656", 1
+    if name == "single_q4k":
+        return wl.single_q4k(), "single_q4k_256x6656", 1
+    return wl.kv_pair() + wl.kv_pair(swapped=True), "kv_pair_q6k_q5k_ntok%d" % ntok, ntok
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kqgen
+    import quant_matvec_amd as kq
+
+    if not os.path.exists(kq.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    kq.load()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    launches, wname, ntok = build_workload(args.workload, args.ntok)
+    print("[bench] generating %s (%d launches)" % (wname, len(launches)), file=sys.stderr, flush=True)
+
+    # ---- inputs resident in HBM
+    sets = []
+    weight_bytes = 0
+    algo_bytes = 0
+    keep = []
+    for launch in launches:
+        xs = {}
+        members = []
+        for T in launch:
+            w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+            dw = torch.from_numpy(w.reshape(-1)).to(dev)
+            if T.xkey not in xs:
+                xs[T.xkey] = torch.from_numpy(kqgen.activations(ntok, T.cols, *T.xkey)).to(dev)
+                algo_bytes += ntok * T.cols * 4
+            dy = torch.empty((ntok, T.rows), dtype=torch.float32, device=dev)
+            keep += [dw, dy]
+            members.append(dict(fmt=T.fmt, w=dw, x=xs[T.xkey], y=dy, rows=T.rows, cols=T.cols))
+            weight_bytes += T.weight_bytes
+            algo_bytes += T.weight_bytes + ntok * T.rows * 4
+        keep += list(xs.values())
+        sets.append(kq.make_set(members))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    n_launch = len(sets)
+
+    def step():
+        for s in sets:
+            kq.kq_matvec_set(s, ntok=ntok, stream=sptr)
+
+    # ---- warmup (also allocates the per-stream workspace outside the timed region)
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, synchronized on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # ---- kernel durations: HIP events around every launch on the launch stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
+    reps = max(1, min(args.steps, 10))
+    durs = []
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        for s, (a, b) in zip(sets, ev):
+            a.record(stream)
+            kq.kq_matvec_set(s, ntok=ntok, stream=sptr)
+            b.record(stream)
+        torch.cuda.synchronize()
+        durs.extend(a.elapsed_time(b) * 1e3 for a, b in ev)   # microseconds
+    avg_launch_us = float(np.mean(durs))
+    bytes_per_launch = algo_bytes / n_launch
+    achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
+
+    ms_per_step = elapsed / args.steps * 1e3
+    value = weight_bytes * args.steps / elapsed / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(launches, ntok, args.cpu_seconds)
+
+    out = {
+        "metric": "effective weight GB/s (and % of HBM peak) + us per QKV+gate set, ntok=1",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded k-quant blocks and N(0,1) activations)",
+        "config": {"workload": wname, "launches_per_step": n_launch, "weight_bytes_per_step": weight_bytes,
+                   "ntok": ntok, "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+                   "us_per_launch_end_to_end": round(ms_per_step * 1e3 / n_launch, 3),
+                   "us_per_launch_kernel": round(avg_launch_us, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kq_matvec_kernel<1>", "bytes_per_launch": int(bytes_per_launch)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(launches, ntok, budget_s):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    whole tensors, layer by layer, until about budget_s seconds of work."""
+    import numpy as np
+
+    import kqgen
+    import oracle
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
+    threads = max(1, min(threads, 16))
+    done_bytes = 0
+    spent = 0.0
+    tensors = 0
+    for launch in launches:
+        for T in launch:
+            w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+            x = kqgen.activations(ntok, T.cols, *T.xkey)
+            t0 = time.perf_counter()
+            oracle.matvec(T.fmt, w, T.rows, T.cols, x, nthreads=threads)
+            spent += time.perf_counter() - t0
+            done_bytes += T.weight_bytes
+            tensors += 1
+            if spent >= budget_s:
+                break
+        if spent >= budget_s:
+            break
+    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d whole tensors (%d weight bytes) of the same workload, ntok=%d, %.1f s"
+                      % (tensors, done_bytes, ntok, spent)}
+
+
+if __name__ == "__main__":
+    main()

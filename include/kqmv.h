@@ -1,0 +1,162 @@
+/*
+ * kqmv.h -- C ABI of the k-quant decode matvec library (libkqmv.so) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes y = W x for weight matrices stored as k-quant
+ * super-blocks, dequantizing every weight on the fly inside the kernel and
+ * never writing a dequantized weight to memory (muser-book Ch 13 "The QKV +
+ * gate matvec family", section 13.1).  Formats and byte layouts are those of
+ * muser-book Ch 6 "The kquant family on the reference lane": Q4_K (section
+ * 6.2, Figures 6.2-6.3), Q5_K and Q6_K (section 6.4, Figures 6.4-6.5).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named w, x, y, *_out are DEVICE pointers (hipMalloc'd memory
+ *     or any device-accessible allocation).  kq_tensor arrays are HOST
+ *     memory and are copied into the launch, so they may be freed on return.
+ *   - The caller owns all device memory.  Work is enqueued on `stream` (a
+ *     hipStream_t, NULL = the default stream) and completes asynchronously;
+ *     no entry point synchronizes.  Results may be read after the stream is
+ *     synchronized.
+ *   - Every check runs on the host before any HIP call; a failed check
+ *     returns a negative KQ_ERR_* code and enqueues nothing.  A launch
+ *     failure reported by the HIP runtime returns KQ_ERR_HIP.  Nothing is
+ *     printed and no exception crosses the ABI.
+ *   - Weights: a row-major matrix of `rows` rows, each one contiguous run of
+ *     cols/256 super-blocks (muser-book Ch 13 section 13.3; Ch 6 section
+ *     6.6), i.e. rows * kq_row_bytes(fmt, cols) bytes.  `w` may point into a
+ *     larger allocation (a view into a mapped model arena) but must be
+ *     16-byte aligned.
+ *   - Activations: x is float32 [ntok][ldx], y is float32 [ntok][ldy]
+ *     (plane t of x is x + t*ldx; ldx >= cols, ldy >= rows).  x must be
+ *     16-byte aligned and ldx a multiple of 4; y must be 4-byte aligned.
+ *   - Results are deterministic run to run.  Each output equals the exact
+ *     sum of W[i,j]*x[j] within a few float32 rounding steps (the kernels
+ *     accumulate in float32 with the per-sub-block scale applied once per
+ *     sub-block), so they are not bitwise equal to another kernel's.
+ *   - Up to 16 devices; calls on one device that run concurrently on
+ *     different streams are safe.  Each (device, stream) pair gets its own
+ *     small workspace (partial sums and counters), allocated with hipMalloc
+ *     on the first call that needs it -- make that first call outside HIP
+ *     graph capture.
+ */
+#ifndef KQMV_H
+#define KQMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* GGUF tensor type ids (muser-book Ch 6 section 6.1, the GgmlType list). */
+enum kq_format { KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14 };
+
+enum kq_status {
+    KQ_OK = 0,
+    KQ_ERR_FORMAT = -1,    /* format is not Q4_K, Q5_K or Q6_K (refused, never converted) */
+    KQ_ERR_COLS = -2,      /* cols <= 0 or not a multiple of 256 */
+    KQ_ERR_ROWS = -3,      /* rows <= 0 */
+    KQ_ERR_NTOK = -4,      /* ntok outside 1..8 */
+    KQ_ERR_NULL = -5,      /* a required pointer is NULL */
+    KQ_ERR_ALIGN = -6,     /* w or x not 16-byte aligned, y not 4-byte aligned */
+    KQ_ERR_STRIDE = -7,    /* ldx < cols, ldx not a multiple of 4, or ldy < rows */
+    KQ_ERR_OVERLAP = -8,   /* an output range overlaps another output or an input */
+    KQ_ERR_SET_SIZE = -9,  /* n outside 1..KQ_MAX_SET */
+    KQ_ERR_HIP = -10,      /* the HIP runtime reported an error */
+    KQ_ERR_TOO_LARGE = -11 /* a size exceeds the kernels' 32-bit index space */
+};
+
+#define KQ_MAX_SET 16
+#define KQ_MAX_NTOK 8
+
+/* One member of a grid-split set. */
+typedef struct kq_tensor {
+    int32_t fmt;          /* enum kq_format */
+    int32_t reserved;     /* must be 0 */
+    const void* w;        /* device weights, rows * kq_row_bytes(fmt, cols) bytes */
+    const float* x;       /* device activations [ntok][ldx] read by this tensor */
+    float* y;             /* device outputs [ntok][ldy] written by this tensor */
+    int64_t rows;
+    int64_t cols;
+    int64_t ldx;
+    int64_t ldy;
+} kq_tensor;
+
+/* Bytes per 256-weight super-block: 144, 176 or 210 (muser-book Ch 6
+ * Figure 6.1); KQ_ERR_FORMAT for any other format. */
+int32_t kq_block_bytes(int32_t fmt);
+
+/* Bytes of one row of `cols` weights: cols/256 * kq_block_bytes(fmt)
+ * (muser-book Ch 6 section 6.6); a negative KQ_ERR_* code on bad input. */
+int64_t kq_row_bytes(int32_t fmt, int64_t cols);
+
+/*
+ * y[t][i] = sum_j W[i,j] * x[t][j] for t < ntok and i < rows
+ * (muser-book Ch 13 section 13.1; ntok columns as the batch-width rungs of
+ * Ch 6 Figure 6.7, served here by one kernel that reads every weight byte
+ * once and uses it ntok times).  ntok in 1..8.
+ * Returns KQ_OK or a negative KQ_ERR_* code.
+ */
+int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols,
+              const float* x, int64_t ldx, float* y, int64_t ldy,
+              int32_t ntok, void* stream);
+
+/*
+ * n independent matvecs in ONE kernel launch (the concurrent Q/K/V/gate set
+ * of muser-book Ch 13 section 13.5, issued as one grid the way the
+ * opus_gdn_qsa audit's gemv_cat splits its grid between tensors).  Each
+ * tensor has its own format, weights, x plane(s) and output; tensors may
+ * share x.  Outputs must be pairwise disjoint and must not overlap any
+ * weights or activations.  Every workgroup works on one tensor only, so
+ * each tensor's result is bitwise equal to a kq_matvec call on it.
+ * n in 1..KQ_MAX_SET, ntok in 1..8 (common to the set).
+ */
+int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream);
+
+/*
+ * Host-only validation of a set (the checks kq_matvec_set runs before any
+ * HIP call).  Makes no HIP call at all.  Returns KQ_OK or the error code
+ * kq_matvec_set would return.
+ */
+int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok);
+
+/*
+ * Debug/test export: integer decode of `nblocks` consecutive super-blocks
+ * starting at w (16-byte aligned), with the same device decoders the matvec
+ * kernels use.  Outputs (device pointers, any may be NULL to skip):
+ *   codes_out  int32 [nblocks][256]: Q4_K 0..15, Q5_K 0..31,
+ *              Q6_K -32..31 (the 6-bit code minus 32)
+ *   scales_out int32 [nblocks][16]: Q4_K/Q5_K sc_0..sc_7 then zeros;
+ *              Q6_K the 16 signed int8 sub-block scales
+ *   mins_out   int32 [nblocks][16]: Q4_K/Q5_K m_0..m_7 then zeros; Q6_K zeros
+ *   d_out, dmin_out float [nblocks]: the f16 headers widened to float
+ *              (Q6_K dmin = 0)
+ * Returns KQ_OK or a negative KQ_ERR_* code.
+ */
+int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks,
+                     int32_t* codes_out, int32_t* scales_out, int32_t* mins_out,
+                     float* d_out, float* dmin_out, void* stream);
+
+/*
+ * Debug/test export: dequantized weights as float32 [rows][ldw]
+ * (ldw >= cols): Q4_K/Q5_K d*sc_j*q - dmin*m_j, Q6_K d*sc_j*q (muser-book
+ * Ch 6 sections 6.2 and 6.4).  Both products are exact in float32 and the
+ * difference is rounded once, so each value is the exact weight correctly
+ * rounded to float32.  The matvec kernels never call this.
+ */
+int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols,
+               float* out, int64_t ldw, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* kq_strerror(int code);
+
+/* ABI version of this header/library pair. */
+int kq_version(void);
+
+#define KQMV_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQMV_H */

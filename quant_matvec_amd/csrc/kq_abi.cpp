@@ -1,0 +1,272 @@
+// kq_abi.cpp -- the extern "C" boundary of libkqmv.so (declared in
+// include/kqmv.h): argument checks, work planning, per-stream workspaces
+// and the calls into the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "kq_plan.h"
+
+namespace kq {
+
+int launch_matvec(const KqLaunch& L, hipStream_t stream);
+int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,
+                  int32_t* mins, float* d, float* dmin, hipStream_t stream);
+int launch_dequant(int32_t fmt, const void* w, int64_t rows, int32_t nb, float* out, int64_t ldw,
+                   hipStream_t stream);
+
+int32_t block_bytes(int32_t fmt) {
+    switch (fmt) {
+    case KQ_Q4_K: return 144;
+    case KQ_Q5_K: return 176;
+    case KQ_Q6_K: return 210;
+    default: return KQ_ERR_FORMAT;
+    }
+}
+
+static int32_t slot_bytes(int32_t fmt) {
+    return fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K : kSlotBytesQ6K;
+}
+
+// Column split of one tensor.  An item stages a few super-block columns of
+// 64 rows (about 27-37 KB), so that a large tensor yields many items and the
+// last items of a launch are short.  Small tensors use shorter items so a
+// launch still has enough workgroups to cover every compute unit.
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* kparts, int32_t* kchunk) {
+    (void)ntok;
+    const int64_t tiles = (rows + kTileRows - 1) / kTileRows;
+    const int64_t nb = cols / 256;
+    int64_t chunk = fmt == KQ_Q4_K ? 4 : fmt == KQ_Q5_K ? 3 : 2;
+    const int64_t want_items = 1024;
+    while (chunk > 1 && tiles * ((nb + chunk - 1) / chunk) < want_items) --chunk;
+    if (chunk > nb) chunk = nb;
+    *kchunk = (int32_t)chunk;
+    *kparts = (int32_t)((nb + chunk - 1) / chunk);
+}
+
+static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
+    return a0 < b1 && b0 < a1;
+}
+
+int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
+    if (n < 1 || n > kMaxSet) return KQ_ERR_SET_SIZE;
+    if (t == nullptr) return KQ_ERR_NULL;
+    if (ntok < 1 || ntok > KQ_MAX_NTOK) return KQ_ERR_NTOK;
+    int64_t items = 0;
+    for (int i = 0; i < n; ++i) {
+        const kq_tensor& T = t[i];
+        if (block_bytes(T.fmt) < 0) return KQ_ERR_FORMAT;
+        if (T.cols <= 0 || T.cols % 256) return KQ_ERR_COLS;
+        if (T.rows <= 0) return KQ_ERR_ROWS;
+        if (!T.w || !T.x || !T.y) return KQ_ERR_NULL;
+        if (T.reserved != 0) return KQ_ERR_FORMAT;
+        if ((reinterpret_cast<uintptr_t>(T.w) & 15) || (reinterpret_cast<uintptr_t>(T.x) & 15) ||
+            (reinterpret_cast<uintptr_t>(T.y) & 3))
+            return KQ_ERR_ALIGN;
+        if (T.ldx < T.cols || (T.ldx & 3) || T.ldy < T.rows) return KQ_ERR_STRIDE;
+        // 32-bit index space of the kernels: a 64-row tile must span < 2^31
+        // bytes, rows and per-plane offsets must fit in int32.
+        const int64_t rb = (T.cols / 256) * block_bytes(T.fmt);
+        if (T.rows > INT32_MAX || rb * kTileRows >= ((int64_t)1 << 31) || T.ldx > ((int64_t)1 << 40) ||
+            T.ldy > ((int64_t)1 << 40))
+            return KQ_ERR_TOO_LARGE;
+        int32_t kp, kc;
+        plan_tensor(T.fmt, T.rows, T.cols, ntok, &kp, &kc);
+        items += ((T.rows + kTileRows - 1) / kTileRows) * kp;
+        if (items > INT32_MAX / 2) return KQ_ERR_TOO_LARGE;
+    }
+    // outputs must not overlap each other or any input (hull of the strided ranges)
+    for (int i = 0; i < n; ++i) {
+        const kq_tensor& A = t[i];
+        const uintptr_t y0 = reinterpret_cast<uintptr_t>(A.y);
+        const uintptr_t y1 = y0 + (uintptr_t)(((int64_t)(ntok - 1) * A.ldy + A.rows) * 4);
+        for (int j = 0; j < n; ++j) {
+            const kq_tensor& B = t[j];
+            const uintptr_t w0 = reinterpret_cast<uintptr_t>(B.w);
+            const uintptr_t w1 = w0 + (uintptr_t)(B.rows * (B.cols / 256) * block_bytes(B.fmt));
+            const uintptr_t x0 = reinterpret_cast<uintptr_t>(B.x);
+            const uintptr_t x1 = x0 + (uintptr_t)(((int64_t)(ntok - 1) * B.ldx + B.cols) * 4);
+            if (ranges_overlap(y0, y1, w0, w1) || ranges_overlap(y0, y1, x0, x1)) return KQ_ERR_OVERLAP;
+            if (j != i) {
+                const uintptr_t z0 = reinterpret_cast<uintptr_t>(B.y);
+                const uintptr_t z1 = z0 + (uintptr_t)(((int64_t)(ntok - 1) * B.ldy + B.rows) * 4);
+                if (ranges_overlap(y0, y1, z0, z1)) return KQ_ERR_OVERLAP;
+            }
+        }
+    }
+    return KQ_OK;
+}
+
+int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPlanSizes* sz) {
+    *L = KqLaunch{};
+    L->n = n;
+    L->ntok = ntok;
+    int32_t items = 0, parts = 0, tiles_split = 0, lds = 0;
+    for (int i = 0; i < n; ++i) {
+        const kq_tensor& T = t[i];
+        KqDesc& D = L->t[i];
+        D.w = static_cast<const uint8_t*>(T.w);
+        D.x = T.x;
+        D.y = T.y;
+        D.ldx = T.ldx;
+        D.ldy = T.ldy;
+        D.nb = (int32_t)(T.cols / 256);
+        D.row_bytes = (int64_t)D.nb * block_bytes(T.fmt);
+        D.rows = (int32_t)T.rows;
+        D.fmt = T.fmt;
+        D.tiles = (int32_t)((T.rows + kTileRows - 1) / kTileRows);
+        plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.kparts, &D.kchunk);
+        D.item_base = items;
+        items += D.tiles * D.kparts;
+        D.part_base = parts;
+        D.tile_base = tiles_split;
+        if (D.kparts > 1) {
+            parts += D.tiles * D.kparts;
+            tiles_split += D.tiles;
+        }
+        if (slot_bytes(T.fmt) > lds) lds = slot_bytes(T.fmt);
+    }
+    L->total_items = items;
+    L->lds_bytes = lds;
+    sz->partial_floats = (size_t)parts * ntok * kTileRows;
+    sz->counters = (size_t)tiles_split;
+    return KQ_OK;
+}
+
+// -------------------------------------------------------------- workspaces
+// One per (device, stream): partial sums and the per-tile arrival counters
+// of the column-split fix-up.  Counters are zeroed when allocated and every
+// launch leaves them zero again.
+struct Workspace {
+    float* partials = nullptr;
+    size_t partial_cap = 0;
+    uint32_t* counters = nullptr;
+    size_t counter_cap = 0;
+};
+
+static std::mutex g_ws_mutex;
+static std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+static int get_workspace(hipStream_t stream, const KqPlanSizes& sz, float** partials, uint32_t** counters) {
+    *partials = nullptr;
+    *counters = nullptr;
+    if (sz.partial_floats == 0 && sz.counters == 0) return KQ_OK;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    Workspace& ws = g_ws[std::make_pair(dev, stream)];
+    if (ws.partial_cap < sz.partial_floats || ws.counter_cap < sz.counters) {
+        if (ws.partials || ws.counters) {
+            if (hipStreamSynchronize(stream) != hipSuccess) return KQ_ERR_HIP;
+            (void)hipFree(ws.partials);
+            (void)hipFree(ws.counters);
+            ws = Workspace{};
+        }
+        size_t pc = sz.partial_floats < (1u << 20) ? (1u << 20) : sz.partial_floats;
+        size_t cc = sz.counters < (1u << 16) ? (1u << 16) : sz.counters;
+        if (hipMalloc(&ws.partials, pc * sizeof(float)) != hipSuccess) return KQ_ERR_HIP;
+        if (hipMalloc(&ws.counters, cc * sizeof(uint32_t)) != hipSuccess) {
+            (void)hipFree(ws.partials);
+            ws = Workspace{};
+            return KQ_ERR_HIP;
+        }
+        if (hipMemsetAsync(ws.counters, 0, cc * sizeof(uint32_t), stream) != hipSuccess) return KQ_ERR_HIP;
+        ws.partial_cap = pc;
+        ws.counter_cap = cc;
+    }
+    *partials = ws.partials;
+    *counters = ws.counters;
+    return KQ_OK;
+}
+
+}  // namespace kq
+
+using namespace kq;
+
+extern "C" {
+
+int32_t kq_block_bytes(int32_t fmt) { return block_bytes(fmt); }
+
+int64_t kq_row_bytes(int32_t fmt, int64_t cols) {
+    const int32_t bb = block_bytes(fmt);
+    if (bb < 0) return KQ_ERR_FORMAT;
+    if (cols <= 0 || cols % 256) return KQ_ERR_COLS;
+    return (cols / 256) * bb;
+}
+
+int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok) {
+    return validate_set(tensors, n, ntok);
+}
+
+int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream) {
+    int rc = validate_set(tensors, n, ntok);
+    if (rc != KQ_OK) return rc;
+    KqLaunch L;
+    KqPlanSizes sz;
+    build_launch(tensors, n, ntok, &L, &sz);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = get_workspace(s, sz, &L.partials, &L.counters);
+    if (rc != KQ_OK) return rc;
+    return launch_matvec(L, s);
+}
+
+int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx,
+              float* y, int64_t ldy, int32_t ntok, void* stream) {
+    kq_tensor t;
+    t.fmt = fmt;
+    t.reserved = 0;
+    t.w = w;
+    t.x = x;
+    t.y = y;
+    t.rows = rows;
+    t.cols = cols;
+    t.ldx = ldx;
+    t.ldy = ldy;
+    return kq_matvec_set(&t, 1, ntok, stream);
+}
+
+int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes_out, int32_t* scales_out,
+                     int32_t* mins_out, float* d_out, float* dmin_out, void* stream) {
+    if (block_bytes(fmt) < 0) return KQ_ERR_FORMAT;
+    if (nblocks <= 0) return KQ_ERR_ROWS;
+    if (!w) return KQ_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(w) & 15) return KQ_ERR_ALIGN;
+    if (nblocks > ((int64_t)1 << 31) * 255) return KQ_ERR_TOO_LARGE;
+    return launch_unpack(fmt, w, nblocks, codes_out, scales_out, mins_out, d_out, dmin_out,
+                         static_cast<hipStream_t>(stream));
+}
+
+int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols, float* out, int64_t ldw, void* stream) {
+    if (block_bytes(fmt) < 0) return KQ_ERR_FORMAT;
+    if (cols <= 0 || cols % 256) return KQ_ERR_COLS;
+    if (rows <= 0) return KQ_ERR_ROWS;
+    if (!w || !out) return KQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(w) & 15) || (reinterpret_cast<uintptr_t>(out) & 3)) return KQ_ERR_ALIGN;
+    if (ldw < cols) return KQ_ERR_STRIDE;
+    if (rows * (cols / 256) > ((int64_t)1 << 31) * 255) return KQ_ERR_TOO_LARGE;
+    return launch_dequant(fmt, w, rows, (int32_t)(cols / 256), out, ldw, static_cast<hipStream_t>(stream));
+}
+
+const char* kq_strerror(int code) {
+    switch (code) {
+    case KQ_OK: return "ok";
+    case KQ_ERR_FORMAT: return "unsupported format (only Q4_K=12, Q5_K=13, Q6_K=14)";
+    case KQ_ERR_COLS: return "cols must be a positive multiple of 256";
+    case KQ_ERR_ROWS: return "rows (or block count) must be positive";
+    case KQ_ERR_NTOK: return "ntok must be in 1..8";
+    case KQ_ERR_NULL: return "null pointer";
+    case KQ_ERR_ALIGN: return "misaligned pointer (w, x need 16 bytes; y 4 bytes)";
+    case KQ_ERR_STRIDE: return "bad leading dimension (ldx >= cols and a multiple of 4; ldy >= rows)";
+    case KQ_ERR_OVERLAP: return "an output overlaps another output or an input";
+    case KQ_ERR_SET_SIZE: return "set size must be in 1..16";
+    case KQ_ERR_HIP: return "HIP runtime error";
+    case KQ_ERR_TOO_LARGE: return "size exceeds the kernels' index space";
+    default: return "unknown status";
+    }
+}
+
+int kq_version(void) { return KQMV_ABI_VERSION; }
+
+}  // extern "C"

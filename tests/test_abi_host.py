@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/kqmv.h declares, and rejects bad arguments before any HIP call
+(the fail-closed admission of muser-book Ch 6 section 6.1).  CPU only: only
+calls that fail validation are made, so no HIP work is ever issued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quant_matvec_amd as kq
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "kqmv.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kq.LIB_PATH):
+        from quant_matvec_amd import build
+        build.build()
+    return kq.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(kq.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_geometry(lib):
+    assert kq.kq_version() == 1
+    assert [kq.kq_block_bytes(f) for f in (12, 13, 14)] == [144, 176, 210]
+    assert kq.kq_row_bytes(12, 6656) == 3744
+    assert kq.kq_row_bytes(13, 6656) == 4576
+    assert kq.kq_row_bytes(14, 6656) == 5460
+    assert lib.kq_block_bytes(2) == -1
+    assert lib.kq_row_bytes(12, 300) == -2
+    assert lib.kq_row_bytes(99, 256) == -1
+    for code in range(-11, 1):
+        assert kq.kq_strerror(code)
+
+
+BASE = 0x7F0000000000   # fake, never dereferenced: every case below fails validation
+
+
+def one(**kw):
+    d = dict(fmt=12, w=BASE, x=BASE + (1 << 30), y=BASE + (2 << 30), rows=256, cols=6656)
+    d.update(kw)
+    return d
+
+
+def status(tensors, ntok=1, n=None):
+    return kq.kq_validate_set(kq.make_set(tensors), ntok, n=n)
+
+
+def test_validation_accepts_a_good_set(lib):
+    assert status([one()]) == 0
+    assert status([one(), one(fmt=14, w=BASE + (3 << 30), y=BASE + (4 << 30))], ntok=8) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(fmt=2), -1), (dict(fmt=15), -1), (dict(reserved=1), -1),
+    (dict(cols=0), -2), (dict(cols=300), -2), (dict(cols=-256), -2),
+    (dict(rows=0), -3), (dict(rows=-5), -3),
+    (dict(w=0), -5), (dict(x=0), -5), (dict(y=0), -5),
+    (dict(w=BASE + 8), -6), (dict(x=BASE + (1 << 30) + 4), -6), (dict(y=BASE + (2 << 30) + 2), -6),
+    (dict(ldx=6000), -7), (dict(ldx=6658), -7), (dict(ldy=100), -7),
+    (dict(y=BASE + 64), -8), (dict(y=BASE + (1 << 30) + 4096), -8),
+    (dict(rows=1 << 32), -11),
+])
+def test_validation_rejects(lib, kw, code):
+    assert status([one(**kw)]) == code
+
+
+def test_validation_set_rules(lib):
+    assert status([one()], ntok=0) == -4
+    assert status([one()], ntok=9) == -4
+    assert status([one()], n=0) == -9
+    assert status([one()] * 17, n=17) == -9
+    # two outputs overlap
+    assert status([one(), one(w=BASE + (3 << 30))]) == -8
+    # outputs of plane t reach y + t*ldy: ntok=2 with ldy=rows overlaps a y placed right after
+    a = one(rows=256)
+    b = one(w=BASE + (3 << 30), y=BASE + (2 << 30) + 256 * 4)
+    assert status([a, b], ntok=1) == 0
+    assert status([a, b], ntok=2) == -8
+    # shared x is fine; y inside another tensor's x is not
+    assert status([one(), one(w=BASE + (3 << 30), y=BASE + (4 << 30))]) == 0
+    assert status([one(), one(w=BASE + (3 << 30), x=BASE + (2 << 30), y=BASE + (4 << 30))]) == -8
+
+
+def test_invalid_calls_fail_before_hip(lib):
+    # these return the validation code without touching the GPU (there is none here)
+    assert lib.kq_matvec(12, BASE, 256, 300, BASE + (1 << 30), 300, BASE + (2 << 30), 256, 1, None) == -2
+    assert lib.kq_matvec(12, BASE, 256, 6656, BASE + (1 << 30), 6656, BASE + (2 << 30), 256, 0, None) == -4
+    assert lib.kq_matvec(13, BASE + 1, 256, 6656, BASE + (1 << 30), 6656, BASE + (2 << 30), 256, 1, None) == -6
+    arr = kq.make_set([one()])
+    assert lib.kq_matvec_set(arr, 0, 1, None) == -9
+    assert lib.kq_unpack_blocks(7, BASE, 1, None, None, None, None, None, None) == -1
+    assert lib.kq_unpack_blocks(12, BASE, 0, None, None, None, None, None, None) == -3
+    assert lib.kq_unpack_blocks(12, BASE + 4, 1, None, None, None, None, None, None) == -6
+    assert lib.kq_dequant(14, BASE, 4, 512, BASE + (1 << 30), 256, None) == -7
+    assert lib.kq_dequant(14, BASE, 4, 500, BASE + (1 << 30), 512, None) == -2
+    with pytest.raises(kq.KqError):
+        kq.kq_matvec(12, BASE, 256, 300, BASE + (1 << 30), BASE + (2 << 30), stream=0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(kq, "_lib", None)
+    monkeypatch.setattr(kq, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        kq.kq_version()

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer decode (codes, scales, mins, headers) and the dequantized float32
+weights are compared bit for bit; matvec outputs per row against the
+binary64 oracle with |y_gpu - y_ref| <= 1e-4 * sum_j|W_ij x_j| + 1e-6.
+Inputs are the seeded synthetic blocks of kqgen.
+"""
+import numpy as np
+import pytest
+
+import kqgen
+import oracle
+import quant_matvec_amd as kq
+from gpu_util import check_tol, dev, gpu_matvec, host, note, torch
+from kqgen import FORMATS, Q4_K, Q5_K, Q6_K
+from kqgen import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    kq.load()
+    oracle.lib()
+
+
+def special_blocks(fmt):
+    """Blocks with subnormal / zero / negative headers and extreme codes."""
+    bb = kqgen.BLOCK_BYTES[fmt]
+    out = []
+    for hdr in (0x0001, 0x03FF, 0x0000, 0x8400, 0x7BFF):   # subnormals, zero, -2^-14, max
+        b = np.zeros(bb, np.uint8)
+        b[:] = 0xFF
+        if fmt == Q6_K:
+            b[208:210] = [hdr & 0xFF, hdr >> 8]
+        else:
+            b[0:2] = [hdr & 0xFF, hdr >> 8]
+            b[2:4] = [0x01, 0x00]
+        out.append(b)
+    out.append(np.zeros(bb, np.uint8))
+    return np.stack(out)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_unpack_bit_exact(fmt):
+    nblocks = 1001          # odd count: Q6_K blocks alternate 4-byte and 2-byte alignment
+    blocks = np.concatenate([kqgen.random_blocks(fmt, nblocks - 6, kqgen.rng_for(500, fmt)), special_blocks(fmt)])
+    note("unpack fmt=%d nblocks=%d" % (fmt, nblocks))
+    t = torch()
+    w = dev(blocks.reshape(-1))
+    codes = t.empty((nblocks, 256), dtype=t.int32, device="cuda")
+    scales = t.empty((nblocks, 16), dtype=t.int32, device="cuda")
+    mins = t.empty((nblocks, 16), dtype=t.int32, device="cuda")
+    d = t.empty(nblocks, dtype=t.float32, device="cuda")
+    dmin = t.empty(nblocks, dtype=t.float32, device="cuda")
+    kq.kq_unpack_blocks(fmt, w, nblocks, codes, scales, mins, d, dmin)
+    codes, scales, mins, d, dmin = (host(v) for v in (codes, scales, mins, d, dmin))
+    for i in range(nblocks):
+        ref = oracle.decode_block(fmt, blocks[i].tobytes())
+        assert np.array_equal(codes[i], ref["codes"]), i
+        assert np.array_equal(scales[i], ref["scale"]), i
+        assert np.array_equal(mins[i], ref["min"]), i
+        assert np.float32(ref["d"]).tobytes() == d[i].tobytes(), i
+        assert np.float32(ref["dmin"]).tobytes() == dmin[i].tobytes(), i
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,cols", [(37, 768), (5, 6656), (2, 256)])
+def test_dequant_bit_exact(fmt, rows, cols):
+    w = kqgen.weights(fmt, rows, cols, 501, fmt, rows, cols)
+    note("dequant fmt=%d rows=%d cols=%d" % (fmt, rows, cols))
+    t = torch()
+    out = t.empty((rows, cols + 8), dtype=t.float32, device="cuda")
+    kq.kq_dequant(fmt, dev(w.reshape(-1)), rows, cols, out, ldw=cols + 8)
+    got = host(out)[:, :cols]
+    ref = oracle.dequant(fmt, w, rows, cols).astype(np.float32)   # exact weight, rounded once
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+SHAPES = [(1, 256), (3, 512), (64, 6656), (65, 768), (130, 2560), (257, 6656), (200, 19968)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,cols", SHAPES)
+def test_matvec_parity(fmt, rows, cols):
+    w = kqgen.weights(fmt, rows, cols, 502, fmt, rows, cols)
+    x = kqgen.activations(1, cols, 503, cols)
+    note("matvec fmt=%d rows=%d cols=%d" % (fmt, rows, cols))
+    y = gpu_matvec(fmt, w, rows, cols, x)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
+    check_tol(y, y_ref, s, "fmt %d %dx%d" % (fmt, rows, cols))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("ntok", [2, 3, 8])
+def test_matvec_ntok(fmt, ntok):
+    rows, cols = 131, 6656
+    w = kqgen.weights(fmt, rows, cols, 504, fmt)
+    x = kqgen.activations(ntok, cols, 505, ntok)
+    note("matvec ntok fmt=%d ntok=%d" % (fmt, ntok))
+    y = gpu_matvec(fmt, w, rows, cols, x, ldx=cols + 4, ldy=rows + 3)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
+    check_tol(y, y_ref, s, "fmt %d ntok %d" % (fmt, ntok))
+    # every column of an ntok call is bitwise the ntok=1 result on that column
+    for t in range(ntok):
+        y1 = gpu_matvec(fmt, w, rows, cols, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+
+
+def test_config1_single_q4k():
+    [[T]] = wl.single_q4k()
+    w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+    x = kqgen.activations(1, T.cols, *T.xkey)
+    note("config single Q4_K 256x6656")
+    y = gpu_matvec(T.fmt, w, T.rows, T.cols, x)
+    y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x)
+    check_tol(y, y_ref, s, "single Q4_K")
+    # run to run: bitwise identical
+    y2 = gpu_matvec(T.fmt, w, T.rows, T.cols, x)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+def _set_inputs(tensors, ntok):
+    ws, xs = {}, {}
+    for T in tensors:
+        ws[T.name] = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+        if T.xkey not in xs:
+            xs[T.xkey] = kqgen.activations(ntok, T.cols, *T.xkey)
+    return ws, xs
+
+
+def _run_set(tensors, ws, xs, ntok):
+    t = torch()
+    dw = {k: dev(v.reshape(-1)) for k, v in ws.items()}
+    dx = {k: dev(v) for k, v in xs.items()}
+    ys = {T.name: t.full((ntok, T.rows), float("nan"), dtype=t.float32, device="cuda") for T in tensors}
+    kq.kq_matvec_set([dict(fmt=T.fmt, w=dw[T.name], x=dx[T.xkey], y=ys[T.name], rows=T.rows, cols=T.cols)
+                      for T in tensors], ntok=ntok)
+    return {k: host(v) for k, v in ys.items()}
+
+
+def test_qkvg_set_matches_oracle_and_singles():
+    tensors = wl.qkvg_set()[0]
+    ws, xs = _set_inputs(tensors, 1)
+    note("qkvg set (4096/256/256/4096 x 6656)")
+    ys = _run_set(tensors, ws, xs, 1)
+    for T in tensors:
+        x = xs[T.xkey]
+        y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, x)
+        check_tol(ys[T.name], y_ref, s, "set " + T.name)
+        single = gpu_matvec(T.fmt, ws[T.name], T.rows, T.cols, x)
+        assert np.array_equal(single.view(np.uint32), ys[T.name].view(np.uint32)), T.name
+
+
+@pytest.mark.parametrize("swapped", [False, True])
+@pytest.mark.parametrize("ntok", [1, 2, 4, 8])
+def test_kv_pair_separate_planes(swapped, ntok):
+    tensors = wl.kv_pair(swapped=swapped)[0]
+    ws, xs = _set_inputs(tensors, ntok)
+    note("kv pair swapped=%s ntok=%d" % (swapped, ntok))
+    ys = _run_set(tensors, ws, xs, ntok)
+    for T, other in ((tensors[0], tensors[1]), (tensors[1], tensors[0])):
+        y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey])
+        check_tol(ys[T.name], y_ref, s, "pair " + T.name)
+        single = gpu_matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey])
+        assert np.array_equal(single.view(np.uint32), ys[T.name].view(np.uint32))
+        # the check can see a tensor that reads the other tensor's x plane:
+        # an oracle fed the wrong plane does not pass it
+        y_wrong, _ = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[other.xkey])
+        with pytest.raises(AssertionError):
+            check_tol(ys[T.name], y_wrong, s, "wrong plane")
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_edge_cases(fmt):
+    rows, cols = 70, 512
+    w = kqgen.weights(fmt, rows, cols, 506, fmt)
+    note("edge cases fmt=%d" % fmt)
+    # zero x gives exactly zero
+    y = gpu_matvec(fmt, w, rows, cols, np.zeros((1, cols), np.float32))
+    assert not y.any()
+    # one-hot x gives a column of W (exactly: one product, one rounding)
+    W = oracle.dequant(fmt, w, rows, cols)
+    for j in (0, 31, 32, 255, 256, 511):
+        x = np.zeros((1, cols), np.float32)
+        x[0, j] = 1.0
+        y = gpu_matvec(fmt, w, rows, cols, x)
+        assert np.array_equal(y[0], W[:, j].astype(np.float32)), j
+    # zero headers give zero rows
+    wz = w.copy().reshape(-1, kqgen.BLOCK_BYTES[fmt])
+    if fmt == Q6_K:
+        wz[:, 208:210] = 0
+    else:
+        wz[:, 0:4] = 0
+    y = gpu_matvec(fmt, wz, rows, cols, kqgen.activations(1, cols, 507))
+    assert not y.any()
+
+
+@pytest.mark.parametrize("fmt", (Q4_K, Q5_K))
+def test_near_cancelling_blocks(fmt):
+    """Deferred scaling rounds d*sc*sum(q x) and dmin*m*sum(x) separately;
+    on blocks where d*sc*q nearly cancels dmin*m the result must still meet
+    the per-row bound."""
+    rows, cols = 64, 2560
+    rng = kqgen.rng_for(508, fmt)
+    w = kqgen.weights(fmt, rows, cols, 509, fmt).reshape(-1, kqgen.BLOCK_BYTES[fmt]).copy()
+    # d = dmin, sc_j = m_j = 8 for all sub-blocks, codes 0..2: W = 8*d*(q-1)
+    w[:, 0:2] = w[:, 2:4]
+    w[:, 4:16] = [8, 8, 8, 8, 8, 8, 8, 8, 0x88, 0x88, 0x88, 0x88]
+    qs0 = 16 if fmt == Q4_K else 48
+    q = rng.choice(3, size=(w.shape[0], 256), p=[0.05, 0.9, 0.05])   # mostly W = 0
+    lo, hi = q[:, :128].reshape(-1, 4, 32), q[:, 128:].reshape(-1, 4, 32)
+    codes = np.concatenate([lo, hi], axis=2)    # per group: 32 low + 32 high elements
+    packed = (codes[:, :, :32] | (codes[:, :, 32:] << 4)).reshape(-1, 128)
+    w[:, qs0:qs0 + 128] = packed.astype(np.uint8)
+    if fmt == Q5_K:
+        w[:, 16:48] = 0
+    x = kqgen.activations(1, cols, 510)
+    note("near-cancelling fmt=%d" % fmt)
+    y = gpu_matvec(fmt, w, rows, cols, x)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
+    check_tol(y, y_ref, s, "near-cancelling")
+
+
+def test_lm_head_scale_q6k_sampled():
+    """The 202,048 x 6656 Q6_K matvec at full size, in the launch the
+    benchmark times; the oracle checks a sample of rows (every row tile's
+    first and last row, the tail tile, and random rows)."""
+    [[T]] = wl.lm_head()
+    note("lm_head Q6_K 202048x6656 (full size)")
+    w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+    x = kqgen.activations(1, T.cols, *T.xkey)
+    y = gpu_matvec(T.fmt, w, T.rows, T.cols, x)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(7)
+    idx = np.unique(np.concatenate([np.arange(0, T.rows, 64), np.arange(63, T.rows, 64),
+                                    np.arange(T.rows - 100, T.rows), rng.integers(0, T.rows, 2000)]))
+    y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, row_idx=idx, nthreads=8)
+    check_tol(y[:, idx], y_ref, s, "lm_head sampled")
+
+
+def test_stream_layers_sampled():
+    """Two layers of the 52-layer stream (a Q4_K and a Q5_K layer) at full
+    size, one set launch each, rows sampled against the oracle."""
+    layers = wl.qkvg_stream(layers=2)
+    for tensors in layers:
+        ws, xs = _set_inputs(tensors, 1)
+        note("stream layer fmt q/gate=%d" % tensors[0].fmt)
+        ys = _run_set(tensors, ws, xs, 1)
+        for T in tensors:
+            idx = np.arange(0, T.rows, 7)
+            y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey], row_idx=idx, nthreads=8)
+            check_tol(ys[T.name][:, idx], y_ref, s, "layer " + T.name)
