@@ -26,24 +26,22 @@ int32_t block_bytes(int32_t fmt) {
     }
 }
 
-static int32_t slot_bytes(int32_t fmt) {
-    return fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K : kSlotBytesQ6K;
+// LDS of one workgroup: the weight slot of one super-block column plus one
+// KB of x per token plane.
+static int32_t slot_bytes(int32_t fmt, int32_t ntok) {
+    return (fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K : kSlotBytesQ6K) + 1024 * ntok;
 }
 
-// Column split of one tensor.  An item stages a few super-block columns of
-// 64 rows (about 27-37 KB), so that a large tensor yields many items and the
-// last items of a launch are short.  Small tensors use shorter items so a
-// launch still has enough workgroups to cover every compute unit.
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* kparts, int32_t* kchunk) {
-    (void)ntok;
-    const int64_t tiles = (rows + kTileRows - 1) / kTileRows;
+// Segment length of one tensor: 2 super-blocks (18-27 KB per 64-row
+// segment), so even a single attention set yields enough segments for a
+// full round of workgroups, while a large matrix needs few partial sums.
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg) {
+    (void)fmt;
+    (void)rows;
     const int64_t nb = cols / 256;
-    int64_t chunk = fmt == KQ_Q4_K ? 4 : fmt == KQ_Q5_K ? 3 : 2;
-    const int64_t want_items = 1024;
-    while (chunk > 1 && tiles * ((nb + chunk - 1) / chunk) < want_items) --chunk;
-    if (chunk > nb) chunk = nb;
-    *kchunk = (int32_t)chunk;
-    *kparts = (int32_t)((nb + chunk - 1) / chunk);
+    const int64_t S = nb < 2 ? nb : 2;
+    *seg = (int32_t)S;
+    *nseg = (int32_t)((nb + S - 1) / S);
 }
 
 static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
@@ -72,9 +70,9 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
         if (T.rows > INT32_MAX || rb * kTileRows >= ((int64_t)1 << 31) || T.ldx > ((int64_t)1 << 40) ||
             T.ldy > ((int64_t)1 << 40))
             return KQ_ERR_TOO_LARGE;
-        int32_t kp, kc;
-        plan_tensor(T.fmt, T.rows, T.cols, ntok, &kp, &kc);
-        items += ((T.rows + kTileRows - 1) / kTileRows) * kp;
+        int32_t ns, sg;
+        plan_tensor(T.fmt, T.rows, T.cols, &ns, &sg);
+        items += ((T.rows + kTileRows - 1) / kTileRows) * ns;
         if (items > INT32_MAX / 2) return KQ_ERR_TOO_LARGE;
     }
     // outputs must not overlap each other or any input (hull of the strided ranges)
@@ -103,7 +101,8 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
     *L = KqLaunch{};
     L->n = n;
     L->ntok = ntok;
-    int32_t items = 0, parts = 0, tiles_split = 0, lds = 0;
+    int64_t cost = 0;
+    int32_t parts = 0, tiles = 0, lds = 0, segs = 0;
     for (int i = 0; i < n; ++i) {
         const kq_tensor& T = t[i];
         KqDesc& D = L->t[i];
@@ -117,21 +116,22 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.rows = (int32_t)T.rows;
         D.fmt = T.fmt;
         D.tiles = (int32_t)((T.rows + kTileRows - 1) / kTileRows);
-        plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.kparts, &D.kchunk);
-        D.item_base = items;
-        items += D.tiles * D.kparts;
+        plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg);
+        D.seg_cost = (int64_t)kTileRows * D.seg * block_bytes(T.fmt);
+        D.cost_base = cost;
+        cost += (int64_t)D.tiles * D.nseg * D.seg_cost;
         D.part_base = parts;
-        D.tile_base = tiles_split;
-        if (D.kparts > 1) {
-            parts += D.tiles * D.kparts;
-            tiles_split += D.tiles;
-        }
-        if (slot_bytes(T.fmt) > lds) lds = slot_bytes(T.fmt);
+        parts += D.tiles * D.nseg;
+        D.tile_base = tiles;
+        tiles += D.tiles;
+        segs += D.tiles * D.nseg;
+        if (slot_bytes(T.fmt, ntok) > lds) lds = slot_bytes(T.fmt, ntok);
     }
-    L->total_items = items;
+    L->total_cost = cost;
+    L->total_segments = segs;
     L->lds_bytes = lds;
     sz->partial_floats = (size_t)parts * ntok * kTileRows;
-    sz->counters = (size_t)tiles_split;
+    sz->counters = (size_t)tiles;
     return KQ_OK;
 }
 

@@ -36,6 +36,9 @@ namespace kq {
 
 typedef const float __attribute__((address_space(4)))* xconst_t;   // scalar-loadable view of x
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;   // global (not flat) byte pointer
+
+__device__ __forceinline__ gbytes_t gbytes(const void* p) { return (gbytes_t)(p); }
 
 constexpr float kTwo24 = 16777216.0f;        // undoes the 2^-24 of a subnormal code
 
@@ -55,91 +58,55 @@ __device__ __forceinline__ float lane_value(float v, int lane) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Sums of x over the sub-blocks of one super-block column, for one token
-// plane xp: SUB = 32 (Q4_K/Q5_K, 8 sums) or 16 (Q6_K, 16 sums).  Lane i adds
-// x[4i..4i+3]; groups of 8 (or 4) lanes are reduced with DPP, so afterwards
-// every lane of group j holds the sum of sub-block j.  The order is fixed,
-// so every workgroup gets the same bits.  The result stays in one VGPR and
-// a sum is moved to an SGPR (readlane) only where it is used.
-template <int SUB>
-__device__ __forceinline__ float subblock_sums(const float* xp) {
-    const int lane = threadIdx.x;
-    float4 v = *reinterpret_cast<const float4*>(xp + 4 * lane);
-    float s = (v.x + v.y) + (v.z + v.w);
-    s = s + dpp_xor1(s);
-    s = s + dpp_xor2(s);
-    if (SUB == 32) s = s + dpp_half_mirror(s);
-    return s;
-}
-
-// Workgroup id -> item.  Workgroups are dealt to the 8 XCDs round-robin;
-// this gives each XCD a contiguous run of items, so the column-split items
-// of one row tile (which share the cache lines at their boundaries) run on
-// the same XCD and meet in its L2.
-__device__ __forceinline__ int xcd_item(int bid, int nblocks) {
+// Workgroup id -> position in the stream.  Workgroups are dealt to the 8
+// XCDs round-robin; this gives each XCD a contiguous run, so neighbouring
+// workgroups (which share a tile, and the cache lines at their boundary)
+// run on the same XCD and meet in its L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     const int xcd = bid & 7, local = bid >> 3;
     const int base = nblocks >> 3, rem = nblocks & 7;
     return xcd * base + min(xcd, rem) + local;
 }
 
-// ------------------------------------------------------------ item context
-struct Item {
-    int tile, kp, r0, rows_here, kb0, kb1;
-};
-
-__device__ __forceinline__ Item make_item(const KqDesc& T, int local) {
-    Item it;
-    it.tile = local / T.kparts;
-    it.kp = local - it.tile * T.kparts;
-    it.r0 = it.tile * kTileRows;
-    it.rows_here = min(kTileRows, T.rows - it.r0);
-    it.kb0 = it.kp * T.kchunk;
-    it.kb1 = min(T.nb, it.kb0 + T.kchunk);
-    return it;
-}
-
-// Write the 64 row results, or hand them to the column-split fix-up: the
-// last item of a row tile to arrive adds all partials in column order.
-template <int NTOK>
-__device__ __forceinline__ void finish_item(const KqDesc& T, const KqLaunch& L, const Item& it,
-                                            const float (&acc)[NTOK]) {
-    const int lane = threadIdx.x;
-    if (T.kparts == 1) {
-        if (lane < it.rows_here) {
-#pragma unroll
-            for (int t = 0; t < NTOK; ++t) T.y[t * T.ldy + it.r0 + lane] = acc[t];
-        }
-        return;
-    }
-    float* tile_parts = L.partials + (size_t)(T.part_base + it.tile * T.kparts) * (NTOK * kTileRows);
-    float* mine = tile_parts + (size_t)it.kp * (NTOK * kTileRows);
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t)
-        __hip_atomic_store(mine + t * kTileRows + lane, acc[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint32_t* ctr = L.counters + T.tile_base + it.tile;
-    uint32_t old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != (uint32_t)(T.kparts - 1)) return;
-    // last arriver: every other item's partials are visible (acq_rel above)
-    float sum[NTOK];
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
-    for (int p = 0; p < T.kparts; ++p) {
-        const float* src = tile_parts + (size_t)p * (NTOK * kTileRows);
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t)
-            sum[t] += __hip_atomic_load(src + t * kTileRows + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (lane < it.rows_here) {
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) T.y[t * T.ldy + it.r0 + lane] = sum[t];
-    }
-    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __device__ __forceinline__ uint4 lds_read4(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t lds_read1(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+// ------------------------------------------------------------ x staging
+// The x values of one super-block column (1 KB per token plane) travel with
+// the weights: lane i loads x[4i..4i+3] of the next column into registers,
+// writes them to the wave's LDS x slot next to the weights, and the lanes
+// then read them back with wave-uniform addresses (an LDS broadcast read).
+// On the way the wave forms the sums of x over each sub-block (32 elements
+// for Q4_K/Q5_K, 16 for Q6_K) with DPP: afterwards every lane of group j
+// holds the sum of sub-block j, in a fixed order.
+template <int NTOK>
+struct XStage {
+    float4 v[NTOK];
+    __device__ __forceinline__ void load(const KqDesc& T, int b) {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t)
+            v[t] = __builtin_bit_cast(float4, *(const __attribute__((address_space(1))) u32x4*)(
+                                                  gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane)));
+    }
+    template <int SUB>
+    __device__ __forceinline__ void commit(uint8_t* xslot, float (&sx)[NTOK]) const {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            reinterpret_cast<float4*>(xslot + 1024 * t)[lane] = v[t];
+            float s = (v[t].x + v[t].y) + (v[t].z + v[t].w);
+            s = s + dpp_xor1(s);
+            s = s + dpp_xor2(s);
+            if (SUB == 32) s = s + dpp_half_mirror(s);
+            sx[t] = s;
+        }
+    }
+};
+
+__device__ __forceinline__ float4 xread(const uint8_t* xslot, int t, int e) {
+    return *reinterpret_cast<const float4*>(xslot + 1024 * t + 4 * e);
+}
 
 // ------------------------------------------------------------ Q4_K / Q5_K
 // Block of 144 (Q4_K) or 176 (Q5_K) bytes = 9 or 11 16-byte chunks.
@@ -149,12 +116,14 @@ struct K45 {
     static constexpr int BB = (FMT == KQ_Q4_K) ? 144 : 176;
     static constexpr int C = BB / 16;                          // chunks per row = uint4 staged per lane
     static constexpr int QS_OFF = (FMT == KQ_Q4_K) ? 16 : 48;  // byte offset of qs
+    static constexpr int SUB = 32;
+    static constexpr int WSLOT = kTileRows * BB;
 };
 
 // One group g of a block: sub-blocks 2g (low nibbles) and 2g+1 (high).
 template <int FMT, int NTOK, int G>
 __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&qh)[8], const K4Scales& S,
-                                          xconst_t xb, int64_t ldx, const float (&sx)[NTOK],
+                                          const uint8_t* xslot, const float (&sx)[NTOK],
                                           float (&ts_e)[NTOK], float (&ts_o)[NTOK], float (&tm)[NTOK]) {
     uint32_t qs[8];
     {
@@ -174,15 +143,15 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
         const int e = 64 * G + 4 * k;
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
-            xconst_t xt = xb + t * ldx;
-            al[t] = __builtin_fmaf((float)half_lo(p.lo02), xt[e + 0], al[t]);
-            al[t] = __builtin_fmaf((float)half_lo(p.lo13), xt[e + 1], al[t]);
-            al[t] = __builtin_fmaf((float)half_hi(p.lo02), xt[e + 2], al[t]);
-            al[t] = __builtin_fmaf((float)half_hi(p.lo13), xt[e + 3], al[t]);
-            ah[t] = __builtin_fmaf((float)half_lo(p.hi02), xt[e + 32], ah[t]);
-            ah[t] = __builtin_fmaf((float)half_lo(p.hi13), xt[e + 33], ah[t]);
-            ah[t] = __builtin_fmaf((float)half_hi(p.hi02), xt[e + 34], ah[t]);
-            ah[t] = __builtin_fmaf((float)half_hi(p.hi13), xt[e + 35], ah[t]);
+            const float4 xl = xread(xslot, t, e), xh = xread(xslot, t, e + 32);
+            al[t] = __builtin_fmaf((float)half_lo(p.lo02), xl.x, al[t]);
+            al[t] = __builtin_fmaf((float)half_lo(p.lo13), xl.y, al[t]);
+            al[t] = __builtin_fmaf((float)half_hi(p.lo02), xl.z, al[t]);
+            al[t] = __builtin_fmaf((float)half_hi(p.lo13), xl.w, al[t]);
+            ah[t] = __builtin_fmaf((float)half_lo(p.hi02), xh.x, ah[t]);
+            ah[t] = __builtin_fmaf((float)half_lo(p.hi13), xh.y, ah[t]);
+            ah[t] = __builtin_fmaf((float)half_hi(p.hi02), xh.z, ah[t]);
+            ah[t] = __builtin_fmaf((float)half_hi(p.hi13), xh.w, ah[t]);
         }
     }
     const float sc0 = (float)k4_sc(S, 2 * G), sc1 = (float)k4_sc(S, 2 * G + 1);
@@ -196,50 +165,61 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
     }
 }
 
-template <int FMT, int NTOK>
-__device__ __forceinline__ void item_k45(const KqDesc& T, const KqLaunch& L, const Item& it, uint8_t* slot) {
-    constexpr int C = K45<FMT>::C;
-    constexpr int BB = K45<FMT>::BB;
-    const int lane = threadIdx.x;
-    const uint8_t* base = T.w + (size_t)it.r0 * T.row_bytes;
-
-    // staging: 16-byte chunk q = 64*i + lane of the column -> row q / C, chunk q % C;
-    // in LDS it lands at byte 16*q = row*BB + 16*chunk.
-    uint4 stg[C];
+// Per-lane staging offsets of a 64-row column: 16-byte chunk q = 64*i + lane
+// of the column is row q / C, chunk q % C, at byte offset row*row_bytes +
+// 16*chunk from the tile's first row; in LDS it lands at byte 16*q =
+// row*BB + 16*chunk.
+template <int C>
+struct K45Offsets {
     uint32_t off[C];
-    const int nlive = it.rows_here * C;     // chunks that belong to existing rows
+    __device__ __forceinline__ void init(const KqDesc& T) {
+        int lane = threadIdx.x;
+        // opaque to the optimizer, so these per-format offsets are formed
+        // here and not hoisted to the kernel entry for every format
+        asm volatile("" : "+v"(lane));
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-        const int q = 64 * i + lane;
-        const int r = q / C, c = q - (q / C) * C;
-        off[i] = (uint32_t)r * (uint32_t)T.row_bytes + 16u * c;
-        stg[i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < C; ++i) {
+            const int q = 64 * i + lane;
+            const int r = q / C, c = q - (q / C) * C;
+            off[i] = (uint32_t)r * (uint32_t)T.row_bytes + 16u * c;
+        }
     }
-    auto stage = [&](int b) {
-        const uint8_t* col = base + (size_t)b * BB;
+};
+
+// Staging and compute of one super-block column of 64 rows.
+template <int FMT, int NTOK>
+struct K45Column {
+    static constexpr int C = K45<FMT>::C;
+    static constexpr int BB = K45<FMT>::BB;
+    typedef K45Offsets<C> Offsets;
+    uint4 stg[C];
+    XStage<NTOK> xs;
+
+    // Loads are branch-free: chunks of rows past the end of the tensor (in
+    // its last tile) are clamped to the last chunk of its last row, which
+    // every such chunk exceeds, so they read valid memory whose values are
+    // never used.
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b) {
+        const int rows_here = min(kTileRows, T.rows - tile * kTileRows);
+        const uint32_t max_off = (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C - 1);
+        gbytes_t col = gbytes(T.w) + (size_t)tile * kTileRows * T.row_bytes + (size_t)b * BB;
 #pragma unroll
         for (int i = 0; i < C; ++i)
-            if (64 * i + lane < nlive)
-                stg[i] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(col + off[i])));
-    };
-
-    float acc[NTOK];
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
-    const uint8_t* row = slot + lane * BB;
-
-    stage(it.kb0);
-    for (int b = it.kb0; b < it.kb1; ++b) {
-        __syncthreads();                            // earlier reads of the slot are done
+            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
+        xs.load(T, b);
+    }
+    __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
+        const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
-        if (b + 1 < it.kb1) stage(b + 1);           // next column in flight during this one
-
-        float sx[NTOK];
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) sx[t] = subblock_sums<32>(T.x + t * T.ldx + 256 * b);
-
-        __syncthreads();                            // slot written
+        xs.template commit<32>(slot + K45<FMT>::WSLOT, sx);
+    }
+    // acc[t] += this column's contribution for the lane's row
+    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
+                                                   const float (&sx)[NTOK], float (&acc)[NTOK]) {
+        (void)T; (void)tile; (void)b;
+        const uint8_t* row = slot + threadIdx.x * BB;
+        const uint8_t* xslot = slot + K45<FMT>::WSLOT;
         const uint4 hdr = lds_read4(row);
         uint32_t qh[8];
         if constexpr (FMT == KQ_Q5_K) {
@@ -252,17 +232,16 @@ __device__ __forceinline__ void item_k45(const KqDesc& T, const KqLaunch& L, con
         }
         const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
         const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-        xconst_t xb = (xconst_t)(T.x) + 256 * b;
         float ts_e[NTOK], ts_o[NTOK], tm[NTOK];
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) { ts_e[t] = 0.0f; ts_o[t] = 0.0f; tm[t] = 0.0f; }
-        k45_group<FMT, NTOK, 0>(row, qh, S, xb, T.ldx, sx, ts_e, ts_o, tm);
+        k45_group<FMT, NTOK, 0>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
         __builtin_amdgcn_sched_barrier(0);
-        k45_group<FMT, NTOK, 1>(row, qh, S, xb, T.ldx, sx, ts_e, ts_o, tm);
+        k45_group<FMT, NTOK, 1>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
         __builtin_amdgcn_sched_barrier(0);
-        k45_group<FMT, NTOK, 2>(row, qh, S, xb, T.ldx, sx, ts_e, ts_o, tm);
+        k45_group<FMT, NTOK, 2>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
         __builtin_amdgcn_sched_barrier(0);
-        k45_group<FMT, NTOK, 3>(row, qh, S, xb, T.ldx, sx, ts_e, ts_o, tm);
+        k45_group<FMT, NTOK, 3>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
         const float d24 = d * kTwo24;
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
@@ -271,8 +250,7 @@ __device__ __forceinline__ void item_k45(const KqDesc& T, const KqLaunch& L, con
             acc[t] = __builtin_fmaf(-dmin, tm[t], acc[t]);
         }
     }
-    finish_item<NTOK>(T, L, it, acc);
-}
+};
 
 // -------------------------------------------------------------------- Q6_K
 // 210-byte block: ql[128], qh[64], sc[16] (int8), d (f16, last).  A block
@@ -295,7 +273,7 @@ __device__ __forceinline__ void q6_read4(const uint8_t* row, int i, uint32_t sh,
 
 template <int NTOK, int N, int KH>
 __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, const uint32_t (&scw)[4],
-                                               xconst_t xb, int64_t ldx, const float (&sx)[NTOK],
+                                               const uint8_t* xslot, const float (&sx)[NTOK],
                                                float (&tl)[NTOK], float (&th)[NTOK]) {
     uint32_t A[4], B[4], H[4];
     q6_read4(row, 16 * N + 4 * KH, sh, A);          // ql bytes 64N + 16KH ..
@@ -315,11 +293,11 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
             const int e = 128 * N + 32 * c + 4 * k;
 #pragma unroll
             for (int t = 0; t < NTOK; ++t) {
-                xconst_t xt = xb + t * ldx;
-                a[c][t] = __builtin_fmaf((float)half_lo(p.c02[c]), xt[e + 0], a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_lo(p.c13[c]), xt[e + 1], a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_hi(p.c02[c]), xt[e + 2], a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_hi(p.c13[c]), xt[e + 3], a[c][t]);
+                const float4 xv = xread(xslot, t, e);
+                a[c][t] = __builtin_fmaf((float)half_lo(p.c02[c]), xv.x, a[c][t]);
+                a[c][t] = __builtin_fmaf((float)half_lo(p.c13[c]), xv.y, a[c][t]);
+                a[c][t] = __builtin_fmaf((float)half_hi(p.c02[c]), xv.z, a[c][t]);
+                a[c][t] = __builtin_fmaf((float)half_hi(p.c13[c]), xv.w, a[c][t]);
             }
         }
     }
@@ -338,98 +316,271 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     }
 }
 
-template <int NTOK>
-__device__ __forceinline__ void item_q6(const KqDesc& T, const KqLaunch& L, const Item& it, uint8_t* slot) {
-    const int lane = threadIdx.x;
-    const uintptr_t tbase = reinterpret_cast<uintptr_t>(T.w) + (uintptr_t)it.r0 * T.row_bytes;
-    const uintptr_t tend = reinterpret_cast<uintptr_t>(T.w) + (uintptr_t)T.rows * T.row_bytes;
-    const bool word_lane = lane < kQ6Words;
-
-    uint32_t stg[kTileRows];
+// Row r of the column: the 53 aligned words from the block's start rounded
+// down to 4 bytes (one load instruction per row, lanes 0..52, addresses
+// uniform).  The tensor's very last block, when it starts 4-byte aligned,
+// ends 2 bytes into its 53rd word; that word is then read as 2 bytes.
+template <bool TAIL>
+__device__ __forceinline__ void q6_stage_rows(uint32_t (&stg)[kTileRows], gbytes_t gw, int64_t start,
+                                              int64_t row_bytes, int rows_here, uint32_t lane4) {
+    const bool word_lane = lane4 < 4 * kQ6Words;
 #pragma unroll
-    for (int r = 0; r < kTileRows; ++r) stg[r] = 0;
-    // Row r of the column: 53 aligned words from the block start rounded down
-    // to 4 bytes.  Only the tensor's very last block can end 2 bytes short of
-    // its last word; that word is then read as 2 bytes.
-    auto stage = [&](int b) {
-#pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
-            if (r < it.rows_here) {
-                const uintptr_t a = (tbase + (uintptr_t)r * T.row_bytes + 210u * (uintptr_t)b) & ~(uintptr_t)3;
-                const uint8_t* p = reinterpret_cast<const uint8_t*>(a) + 4 * lane;
-                if (a + 4 * kQ6Words <= tend) {
-                    if (word_lane) stg[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-                } else {
-                    if (lane < kQ6Words - 1) stg[r] = *reinterpret_cast<const uint32_t*>(p);
-                    else if (lane == kQ6Words - 1) stg[r] = *reinterpret_cast<const uint16_t*>(p);
-                }
+    for (int r = 0; r < kTileRows; ++r) {
+        if (r < rows_here) {                          // uniform: rows past the tensor's end are skipped
+            gbytes_t rowp = gw + (start & ~(int64_t)3);
+            const __attribute__((address_space(1))) uint32_t* p =
+                (const __attribute__((address_space(1))) uint32_t*)(rowp + lane4);
+            if (!TAIL || r != rows_here - 1) {
+                if (word_lane) stg[r] = *p;
+            } else {
+                if (lane4 < 4 * (kQ6Words - 1)) stg[r] = *p;
+                else if (lane4 == 4 * (kQ6Words - 1)) stg[r] = *(const __attribute__((address_space(1))) uint16_t*)p;
             }
         }
-    };
+        start += row_bytes;
+    }
+}
 
-    float acc[NTOK];
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
-    const uint8_t* row = slot + lane * kQ6LdsRow;
-    const bool even_nb = (T.nb & 1) == 0;
+struct Q6Offsets {
+    __device__ __forceinline__ void init(const KqDesc& T) { (void)T; }
+};
 
-    stage(it.kb0);
-    for (int b = it.kb0; b < it.kb1; ++b) {
-        __syncthreads();
-        if (word_lane) {
+template <int NTOK>
+struct Q6Column {
+    static constexpr int SUB = 16;
+    static constexpr int WSLOT = kTileRows * kQ6LdsRow;
+    typedef Q6Offsets Offsets;
+    uint32_t stg[kTileRows];
+    XStage<NTOK> xs;
+
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b) {
+        (void)o;
+        const int r0 = tile * kTileRows;
+        const int rows_here = min(kTileRows, T.rows - r0);
+        const uint32_t lane4 = 4u * threadIdx.x;
+        const int64_t start = (int64_t)r0 * T.row_bytes + 210 * (int64_t)b;
+        const int64_t last = (int64_t)(r0 + rows_here - 1) * T.row_bytes + 210 * (int64_t)b;
+        const bool tail = (r0 + rows_here == T.rows) && (b == T.nb - 1) && ((last & 3) == 0);
+        if (!tail) q6_stage_rows<false>(stg, gbytes(T.w), start, T.row_bytes, rows_here, lane4);
+        else q6_stage_rows<true>(stg, gbytes(T.w), start, T.row_bytes, rows_here, lane4);
+        xs.load(T, b);
+    }
+    __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
+        const int lane = threadIdx.x;
+        if (lane < kQ6Words) {
 #pragma unroll
             for (int r = 0; r < kTileRows; ++r) reinterpret_cast<uint32_t*>(slot + r * kQ6LdsRow)[lane] = stg[r];
         }
-        if (b + 1 < it.kb1) stage(b + 1);
-
-        float sx[NTOK];
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) sx[t] = subblock_sums<16>(T.x + t * T.ldx + 256 * b);
-
-        __syncthreads();
+        xs.template commit<16>(slot + WSLOT, sx);
+    }
+    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
+                                                   const float (&sx)[NTOK], float (&acc)[NTOK]) {
+        const int lane = threadIdx.x;
+        const uint8_t* row = slot + lane * kQ6LdsRow;
+        const uint8_t* xslot = slot + WSLOT;
         // the block starts 2 bytes into its first staged word when its index
         // in the tensor, (r0+lane)*nb + b, is odd
-        const uint32_t sh = even_nb ? 16u * (uint32_t)(b & 1)
-                                    : 16u * (uint32_t)(((int64_t)(it.r0 + lane) * T.nb + b) & 1);
+        const uint32_t sh = (T.nb & 1) == 0 ? 16u * (uint32_t)(b & 1)
+                                            : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
         uint32_t scw[4];
         q6_read4(row, 48, sh, scw);
         const uint32_t dw = __builtin_amdgcn_alignbit(lds_read1(row + 4 * 53), lds_read1(row + 4 * 52), sh);
         const float d = f16_to_f32(dw & 0xFFFFu);
-        xconst_t xb = (xconst_t)(T.x) + 256 * b;
         float tl[NTOK], th[NTOK];
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
-        q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xb, T.ldx, sx, tl, th);
+        q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, sx, tl, th);
         __builtin_amdgcn_sched_barrier(0);
-        q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xb, T.ldx, sx, tl, th);
+        q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, sx, tl, th);
         __builtin_amdgcn_sched_barrier(0);
-        q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xb, T.ldx, sx, tl, th);
+        q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, sx, tl, th);
         __builtin_amdgcn_sched_barrier(0);
-        q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xb, T.ldx, sx, tl, th);
+        q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, sx, tl, th);
         const float d24 = d * kTwo24;
 #pragma unroll
         for (int t = 0; t < NTOK; ++t)
             acc[t] = __builtin_fmaf(d24, __builtin_fmaf(th[t], 0.0625f, tl[t]), acc[t]);
     }
-    finish_item<NTOK>(T, L, it, acc);
+};
+
+// ------------------------------------------------------------ tile results
+// Write a tile's 64 row results.
+template <int NTOK>
+__device__ __forceinline__ void write_rows(const KqDesc& T, int tile, const float (&v)[NTOK]) {
+    const int lane = threadIdx.x;
+    const int r0 = tile * kTileRows;
+    if (lane < T.rows - r0) {
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) T.y[t * T.ldy + r0 + lane] = v[t];
+    }
 }
 
-// ------------------------------------------------------------ the kernel
+// Segment sum of a shared tile -> its workspace slot.  Partials and counters
+// are only ever touched with device-scope atomic loads and stores, which the
+// hardware keeps coherent across the XCDs' L2 caches (they carry the
+// device-coherence bit), so no L2-wide writeback/invalidate is needed.
 template <int NTOK>
-__global__ __launch_bounds__(64, (NTOK <= 7 ? 3 : 2)) void kq_matvec_kernel(const KqLaunch L) {
+__device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L, int tile, int seg,
+                                              const float (&v)[NTOK]) {
+    const int lane = threadIdx.x;
+    float* dst = L.partials + ((size_t)T.part_base + (size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t)
+        __hip_atomic_store(dst + t * kTileRows + lane, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// This workgroup stored `count` segment sums of a shared tile.  Ordering:
+// the stores are complete (vmcnt drained) before the counter moves, and
+// the last contributor reads the partials only after its increment
+// returned; it adds all segment sums of the tile in order and resets the
+// counter for the next launch.
+template <int NTOK>
+__device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int tile, int count) {
+    const int lane = threadIdx.x;
+    uint32_t* ctr = L.counters + T.tile_base + tile;
+    uint32_t old = 0;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, (uint32_t)count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (old + (uint32_t)count != (uint32_t)T.nseg) return;
+    const float* src = L.partials + ((size_t)T.part_base + (size_t)tile * T.nseg) * (NTOK * kTileRows);
+    float sum[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
+    for (int p = 0; p < T.nseg; ++p) {
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t)
+            sum[t] += __hip_atomic_load(src + ((size_t)p * NTOK + t) * kTileRows + lane, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    }
+    write_rows<NTOK>(T, tile, sum);
+    if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------ a run of segments
+// Segments j0..j1-1 of tensor T (tile-major), one super-block column at a
+// time.  DEPTH columns are in flight: the loads of column i+DEPTH are issued
+// right after column i has been written to LDS, so a workgroup's first
+// DEPTH columns are requested at once.  (Q4_K/Q5_K use DEPTH 2; a Q6_K
+// column needs 64 staging registers per lane, so it uses DEPTH 1.)  The
+// loop state is kept in plain scalars so that it stays in registers.
+//
+// One column: write column `c` to LDS, refill its registers with the column
+// DEPTH ahead, compute, then close the segment / tile where they end.
+// Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0); a column whose
+// segment is >= j1 lies past the end of the run.
+#define KQ_STEP(c)                                                                             \
+    {                                                                                          \
+        __syncthreads();                                /* earlier reads of the slot done */   \
+        float sx[NTOK];                                                                        \
+        (c).commit(slot, sx);                                                                  \
+        const bool row_end = b + 1 == nb;                                                      \
+        const bool seg_end = row_end || (b + 1) % S == 0;                                      \
+        const int ntile = row_end ? tile + 1 : tile;                                           \
+        const int nbb = row_end ? 0 : b + 1;                                                   \
+        const bool has_next = (int64_t)ntile * nseg + nbb / S < j1;                            \
+        if (DEPTH == 1) {                                                                      \
+            if (has_next) (c).stage(T, offs, ntile, nbb);                                      \
+        } else {                                                                               \
+            const bool nrow_end = nbb + 1 == nb;                                               \
+            const int n2tile = nrow_end ? ntile + 1 : ntile;                                   \
+            const int n2b = nrow_end ? 0 : nbb + 1;                                            \
+            if (has_next && (int64_t)n2tile * nseg + n2b / S < j1) (c).stage(T, offs, n2tile, n2b); \
+        }                                                                                      \
+        __syncthreads();                                /* slot written */                     \
+        Col::compute(T, slot, tile, b, sx, acc);                                               \
+        if (seg_end) {                                                                         \
+            if (owned) {                                                                       \
+                _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = tsum[t] + acc[t];   \
+            } else {                                                                           \
+                store_partial<NTOK>(T, L, tile, seg, acc);                                     \
+                ++pending;                                                                     \
+            }                                                                                  \
+            _Pragma("unroll") for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;                    \
+            if (row_end || !has_next) {                                                        \
+                if (owned) {                                                                   \
+                    write_rows<NTOK>(T, tile, tsum);                                           \
+                    _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = 0.0f;           \
+                } else {                                                                       \
+                    arrive<NTOK>(T, L, tile, pending);                                         \
+                    pending = 0;                                                               \
+                }                                                                              \
+            }                                                                                  \
+            seg = row_end ? 0 : seg + 1;                                                       \
+        }                                                                                      \
+        if (!has_next) break;                                                                  \
+        if (row_end) owned = (int64_t)ntile * nseg >= j0 && (int64_t)(ntile + 1) * nseg <= j1; \
+        tile = ntile;                                                                          \
+        b = nbb;                                                                               \
+    }
+
+template <class Col, int NTOK, int DEPTH>
+__device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int64_t j0, int64_t j1,
+                                             uint8_t* slot) {
+    const int S = T.seg, nseg = T.nseg, nb = T.nb;
+    int tile = (int)(j0 / nseg);
+    int seg = (int)(j0 - (int64_t)tile * nseg);
+    int b = seg * S;
+    typename Col::Offsets offs;
+    offs.init(T);
+    float acc[NTOK], tsum[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) { acc[t] = 0.0f; tsum[t] = 0.0f; }
+    int pending = 0;
+    bool owned = (int64_t)tile * nseg >= j0 && (int64_t)(tile + 1) * nseg <= j1;
+    Col c0;
+    c0.stage(T, offs, tile, b);
+    if constexpr (DEPTH == 2) {
+        Col c1;
+        {
+            const bool row_end = b + 1 == nb;
+            const int ntile = row_end ? tile + 1 : tile;
+            const int nbb = row_end ? 0 : b + 1;
+            if ((int64_t)ntile * nseg + nbb / S < j1) c1.stage(T, offs, ntile, nbb);
+        }
+        while (true) {
+            KQ_STEP(c0)
+            KQ_STEP(c1)
+        }
+    } else {
+        while (true) {
+            KQ_STEP(c0)
+        }
+    }
+}
+#undef KQ_STEP
+
+// ------------------------------------------------------------ the kernel
+// Persistent grid: workgroup w owns the segments whose first weight byte
+// lies in [w*B/P, (w+1)*B/P) of the launch (B bytes, P workgroups).
+template <int NTOK>
+__global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_slot[];
-    const int item = xcd_item(blockIdx.x, gridDim.x);
-    int ti = 0;
-#pragma unroll 1
-    for (int i = 1; i < L.n; ++i)
-        if (item >= L.t[i].item_base) ti = i;
-    const KqDesc& T = L.t[ti];
-    const Item it = make_item(T, item - T.item_base);
     uint8_t* slot = reinterpret_cast<uint8_t*>(kq_slot);
-    switch (T.fmt) {
-    case KQ_Q4_K: item_k45<KQ_Q4_K, NTOK>(T, L, it, slot); break;
-    case KQ_Q5_K: item_k45<KQ_Q5_K, NTOK>(T, L, it, slot); break;
-    default: item_q6<NTOK>(T, L, it, slot); break;
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t c0 = L.total_cost * w / L.grid;
+    const int64_t c1 = L.total_cost * (w + 1) / L.grid;
+#pragma unroll 1
+    for (int i = 0; i < L.n; ++i) {
+        const KqDesc T = L.t[i];          // one batch of scalar loads, then registers
+        const int64_t nsegs = (int64_t)T.tiles * T.nseg;
+        // first segment whose start cost cost_base + j*seg_cost is >= c
+        auto first_at = [&](int64_t c) -> int64_t {
+            const int64_t rel = c - T.cost_base;
+            if (rel <= 0) return 0;
+            const int64_t j = (rel + T.seg_cost - 1) / T.seg_cost;
+            return j < nsegs ? j : nsegs;
+        };
+        const int64_t j0 = first_at(c0), j1 = first_at(c1);
+        if (j0 >= j1) continue;
+        switch (T.fmt) {
+        case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, 2>(T, L, j0, j1, slot); break;
+        case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, 2>(T, L, j0, j1, slot); break;
+        default: run_segments<Q6Column<NTOK>, NTOK, 1>(T, L, j0, j1, slot); break;
+        }
     }
 }
 
@@ -582,20 +733,57 @@ __global__ void kq_dequant_kernel(int32_t fmt, const uint8_t* w, int64_t rows, i
 }
 
 // ------------------------------------------------------------ launchers
-int launch_matvec(const KqLaunch& L, hipStream_t stream) {
-    dim3 grid(L.total_items), block(64);
-    const size_t lds = (size_t)L.lds_bytes;
-    switch (L.ntok) {
-    case 1: hipLaunchKernelGGL(kq_matvec_kernel<1>, grid, block, lds, stream, L); break;
-    case 2: hipLaunchKernelGGL(kq_matvec_kernel<2>, grid, block, lds, stream, L); break;
-    case 3: hipLaunchKernelGGL(kq_matvec_kernel<3>, grid, block, lds, stream, L); break;
-    case 4: hipLaunchKernelGGL(kq_matvec_kernel<4>, grid, block, lds, stream, L); break;
-    case 5: hipLaunchKernelGGL(kq_matvec_kernel<5>, grid, block, lds, stream, L); break;
-    case 6: hipLaunchKernelGGL(kq_matvec_kernel<6>, grid, block, lds, stream, L); break;
-    case 7: hipLaunchKernelGGL(kq_matvec_kernel<7>, grid, block, lds, stream, L); break;
-    default: hipLaunchKernelGGL(kq_matvec_kernel<8>, grid, block, lds, stream, L); break;
+// Resident one-wave workgroups per compute unit for this kernel and LDS
+// size (queried once per device, token count and LDS size).
+template <int NTOK>
+static int resident_per_cu(int lds_bytes) {
+    int dev = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    static int cache[16][9][4] = {};     // [device][ntok][lds class]
+    const int cls = lds_bytes <= 12 * 1024 ? 0 : lds_bytes <= 20 * 1024 ? 1 : lds_bytes <= 28 * 1024 ? 2 : 3;
+    int& c = cache[dev & 15][NTOK][cls];
+    if (c == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kq_matvec_kernel<NTOK>, 64, lds_bytes) != hipSuccess ||
+            per_cu <= 0)
+            per_cu = 1;
+        c = per_cu;
     }
+    return c;
+}
+
+static int compute_units() {
+    static int cus[16] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int& c = cus[dev & 15];
+    if (c == 0 && hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) c = 0;
+    return c;
+}
+
+template <int NTOK>
+static int launch_t(KqLaunch L, hipStream_t stream) {
+    const int cus = compute_units();
+    if (cus <= 0) return KQ_ERR_HIP;
+    const int per_cu = resident_per_cu<NTOK>(L.lds_bytes);
+    int grid = per_cu * cus;
+    if (grid > L.total_segments) grid = L.total_segments;
+    if (grid < 1) grid = 1;
+    L.grid = grid;
+    hipLaunchKernelGGL(kq_matvec_kernel<NTOK>, dim3(grid), dim3(64), (size_t)L.lds_bytes, stream, L);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+int launch_matvec(const KqLaunch& L, hipStream_t stream) {
+    switch (L.ntok) {
+    case 1: return launch_t<1>(L, stream);
+    case 2: return launch_t<2>(L, stream);
+    case 3: return launch_t<3>(L, stream);
+    case 4: return launch_t<4>(L, stream);
+    case 5: return launch_t<5>(L, stream);
+    case 6: return launch_t<6>(L, stream);
+    case 7: return launch_t<7>(L, stream);
+    default: return launch_t<8>(L, stream);
+    }
 }
 
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,

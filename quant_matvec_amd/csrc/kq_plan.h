@@ -2,14 +2,22 @@
 // kernel launcher.  Plain C++ (no HIP types), so the planning and the
 // argument checks can be exercised on a machine without a GPU.
 //
-// Work decomposition.  A workgroup is one 64-lane wave and processes one
-// ITEM: 64 consecutive rows of one tensor (lane i owns row r0+i) over a
-// contiguous range of `kchunk` super-block columns.  A tensor with
-// kparts > 1 is split along the columns; its items write per-row partial
-// sums to a workspace, and the last item of a row tile to finish adds the
-// partials in column order and writes y.  The plan of a tensor depends only
-// on its own (format, rows, cols, ntok), never on the other members of a
-// set, so a tensor computes bitwise the same result alone or in a set.
+// Work decomposition.  Rows are taken 64 at a time (a TILE: one row per
+// lane of a wave64).  Each tile row is cut into SEGMENTS of S consecutive
+// super-blocks; the segments of a tensor are numbered tile-major.  The row
+// results of a tile are the ordered sum ((0 + seg_0) + seg_1) + ... of its
+// segment sums, each segment accumulated block by block.  S depends only on
+// the tensor's own (format, rows, cols), so a tensor computes bitwise the
+// same result alone or in a set, and whatever workgroup does the work.
+//
+// The launch is a persistent grid of P one-wave workgroups (about one full
+// round of resident waves).  Workgroup w streams the contiguous run of
+// segments whose starting byte falls in [w*B/P, (w+1)*B/P) of the launch's
+// B weight bytes, prefetching one super-block column ahead across segment
+// and tile boundaries.  A tile whose segments all belong to one workgroup is
+// summed in registers and written directly; a tile shared by workgroups has
+// its segment sums written to a per-stream workspace, and the last
+// contributor (an arrival counter per tile) adds them in order.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -34,26 +42,29 @@ struct KqDesc {
     float* y;
     int64_t ldx, ldy;
     int64_t row_bytes;
+    int64_t cost_base;  // weight bytes of the launch before this tensor (segment units)
+    int64_t seg_cost;   // bytes of one full segment: 64 * S * block_bytes
     int32_t rows;
     int32_t nb;         // super-blocks per row
     int32_t fmt;
     int32_t tiles;      // ceil(rows / 64)
-    int32_t kparts;     // column splits per row tile
-    int32_t kchunk;     // super-blocks per split (the last may be shorter)
-    int32_t item_base;  // first workgroup of this tensor in the grid
-    int32_t part_base;  // first partial-sum slot (in items) in the workspace
+    int32_t nseg;       // segments per tile row
+    int32_t seg;        // S: super-blocks per segment (the last one of a row may be shorter)
+    int32_t part_base;  // first partial-sum slot (one per segment) in the workspace
     int32_t tile_base;  // first counter in the workspace
-    int32_t pad;
 };
 
 struct KqLaunch {
     KqDesc t[kMaxSet];
-    float* partials;      // workspace: [items of split tensors][ntok][64]
-    uint32_t* counters;   // workspace: one per row tile of split tensors, zero between calls
+    float* partials;      // workspace: [segments][ntok][64]
+    uint32_t* counters;   // workspace: one per tile, zero between calls
+    int64_t total_cost;   // sum of seg_cost * segments over the set
     int32_t n;
     int32_t ntok;
-    int32_t total_items;
+    int32_t grid;         // persistent workgroups
     int32_t lds_bytes;
+    int32_t total_segments;
+    int32_t pad;
 };
 
 struct KqPlanSizes {
@@ -63,16 +74,15 @@ struct KqPlanSizes {
 
 int32_t block_bytes(int32_t fmt);
 
-// Split of one tensor: sets kparts and kchunk.  Depends on (fmt, rows, cols,
-// ntok) only.
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok,
-                 int32_t* kparts, int32_t* kchunk);
+// Segment length S (super-blocks) of one tensor and the segments per tile
+// row.  Depends on (fmt, rows, cols) only.
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg);
 
 // Checks (no HIP calls) of a set; KQ_OK or a KQ_ERR_* code.
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok);
 
-// Fills `out` (workspace pointers left null) and the workspace sizes.
-// Assumes validate_set passed.
+// Fills `out` (workspace pointers and grid left unset) and the workspace
+// sizes.  Assumes validate_set passed.
 int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out, KqPlanSizes* sizes);
 
 }  // namespace kq
