@@ -28,6 +28,32 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# Sources whose hash ties a committed counter measurement to the kernel it measured.
+KERNEL_SOURCES = ["quant_matvec_amd/csrc/kq_kernels.hip", "quant_matvec_amd/csrc/kq_abi.cpp",
+                  "quant_matvec_amd/csrc/kq_plan.h", "quant_matvec_amd/csrc/kq_decode.h", "include/kqmv.h"]
+
+
+def measured_traffic(wname):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel
+    sources have changed since it was taken."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    digest = h.hexdigest()[:16]
+    for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md")):
+        with open(path) as fh:
+            for line in fh:
+                line = line.strip()
+                if line.startswith("{") and '"traffic_bytes_per_launch"' in line:
+                    rec = json.loads(line)
+                    if rec.get("workload") == wname and rec.get("src_sha256_16") == digest:
+                        return int(rec["traffic_bytes_per_launch"])
+    return None
+
 
 def parse():
     p = argparse.ArgumentParser()
@@ -39,6 +65,8 @@ def parse():
     p.add_argument("--ntok", type=int, default=1, help="kv_pair only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                   help="only run a plain device-to-device copy of BYTES bytes (counter calibration) and exit")
     return p.parse_args()
 
 
@@ -77,6 +105,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, dev)
+        return
+
     launches, wname, ntok = build_workload(args.workload, args.ntok)
     print("[bench] generating %s (%d launches)" % (wname, len(launches)), file=sys.stderr, flush=True)
 
@@ -85,14 +117,17 @@ def main():
     weight_bytes = 0
     algo_bytes = 0
     keep = []
+    host = []      # the same seeded inputs, kept for the CPU baseline
     for launch in launches:
         xs = {}
         members = []
         for T in launch:
             w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+            x = kqgen.activations(ntok, T.cols, *T.xkey)
+            host.append((T, w, x))
             dw = torch.from_numpy(w.reshape(-1)).to(dev)
             if T.xkey not in xs:
-                xs[T.xkey] = torch.from_numpy(kqgen.activations(ntok, T.cols, *T.xkey)).to(dev)
+                xs[T.xkey] = torch.from_numpy(x).to(dev)
                 algo_bytes += ntok * T.cols * 4
             dy = torch.empty((ntok, T.rows), dtype=torch.float32, device=dev)
             keep += [dw, dy]
@@ -144,7 +179,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(launches, ntok, args.cpu_seconds)
+        cpu = cpu_baseline(host, ntok, args.cpu_seconds)
 
     out = {
         "metric": "effective weight GB/s (and % of HBM peak) + us per QKV+gate set, ntok=1",
@@ -164,19 +199,17 @@ def main():
                    "us_per_launch_end_to_end": round(ms_per_step * 1e3 / n_launch, 3),
                    "us_per_launch_kernel": round(avg_launch_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wname),
                      "kernel": "kq_matvec_kernel<1>", "bytes_per_launch": int(bytes_per_launch)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(launches, ntok, budget_s):
+def cpu_baseline(host, ntok, budget_s):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    whole tensors, layer by layer, until about budget_s seconds of work."""
-    import numpy as np
-
-    import kqgen
+    whole tensors in launch order, wrapping around, until about budget_s
+    seconds of oracle time."""
     import oracle
 
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
@@ -184,10 +217,8 @@ def cpu_baseline(launches, ntok, budget_s):
     done_bytes = 0
     spent = 0.0
     tensors = 0
-    for launch in launches:
-        for T in launch:
-            w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
-            x = kqgen.activations(ntok, T.cols, *T.xkey)
+    while spent < budget_s:
+        for T, w, x in host:
             t0 = time.perf_counter()
             oracle.matvec(T.fmt, w, T.rows, T.cols, x, nthreads=threads)
             spent += time.perf_counter() - t0
@@ -195,11 +226,22 @@ def cpu_baseline(launches, ntok, budget_s):
             tensors += 1
             if spent >= budget_s:
                 break
-        if spent >= budget_s:
-            break
     return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d whole tensors (%d weight bytes) of the same workload, ntok=%d, %.1f s"
+            "sample": "%d whole tensors (%d weight bytes) of the same workload in launch order, ntok=%d, %.1f s"
                       % (tensors, done_bytes, ntok, spent)}
+
+
+def copy_calibration(nbytes, dev):
+    """A plain device-to-device copy of nbytes (torch's copy kernel), run a
+    few times: reading its FETCH_SIZE / WRITE_SIZE counters gives the
+    factor between those counters and bytes actually moved."""
+    import torch
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}), flush=True)
 
 
 if __name__ == "__main__":
