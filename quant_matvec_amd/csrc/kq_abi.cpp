@@ -99,7 +99,8 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
 
 int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPlanSizes* sz) {
     *L = KqLaunch{};
-    L->n = n;
+    L->h.n = n;
+    for (int i = 0; i < kMaxSet; ++i) L->h.cost_end[i] = INT64_MAX;
     L->ntok = ntok;
     int64_t cost = 0;
     int32_t parts = 0, tiles = 0, lds = 0, segs = 0;
@@ -118,8 +119,11 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.tiles = (int32_t)((T.rows + kTileRows - 1) / kTileRows);
         plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg);
         D.seg_cost = (int64_t)kTileRows * D.seg * block_bytes(T.fmt);
+        D.inv_seg_cost = 1.0 / (double)D.seg_cost;
         D.cost_base = cost;
         cost += (int64_t)D.tiles * D.nseg * D.seg_cost;
+        D.cost_end = cost;
+        L->h.cost_end[i] = cost;
         D.part_base = parts;
         parts += D.tiles * D.nseg;
         D.tile_base = tiles;
@@ -209,6 +213,11 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = get_workspace(s, sz, &L.partials, &L.counters);
     if (rc != KQ_OK) return rc;
+    for (int i = 0; i < n; ++i) {
+        KqDesc& D = L.t[i];
+        D.partials = L.partials ? L.partials + (size_t)D.part_base * ntok * kTileRows : nullptr;
+        D.counters = L.counters ? L.counters + D.tile_base : nullptr;
+    }
     return launch_matvec(L, s);
 }
 

@@ -36,6 +36,7 @@ namespace kq {
 
 typedef const float __attribute__((address_space(4)))* xconst_t;   // scalar-loadable view of x
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;   // global (not flat) byte pointer
 
 __device__ __forceinline__ gbytes_t gbytes(const void* p) { return (gbytes_t)(p); }
@@ -66,6 +67,24 @@ __device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
     const int xcd = bid & 7, local = bid >> 3;
     const int base = nblocks >> 3, rem = nblocks & 7;
     return xcd * base + min(xcd, rem) + local;
+}
+
+// A copy of a kernel-argument struct fetched in one batch of scalar loads:
+// the words are held in 8-dword groups that one empty asm statement takes as
+// SGPR operands, so every load is issued before any is used (instead of each
+// field being loaded next to its first use, a chain of round trips).
+template <class S>
+__device__ __forceinline__ S load_uniform(const S& src) {
+    static_assert(sizeof(S) == 128, "four 8-dword groups");
+    constexpr int G = sizeof(S) / 32;
+    const u32x8* p = reinterpret_cast<const u32x8*>(&src);
+    u32x8 g[G];
+#pragma unroll
+    for (int k = 0; k < G; ++k) g[k] = p[k];
+    asm volatile("" : : "s"(g[0]), "s"(g[1]), "s"(g[2]), "s"(g[3]));
+    S out;
+    __builtin_memcpy(&out, g, sizeof(S));
+    return out;
 }
 
 __device__ __forceinline__ uint4 lds_read4(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -423,7 +442,7 @@ template <int NTOK>
 __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L, int tile, int seg,
                                               const float (&v)[NTOK]) {
     const int lane = threadIdx.x;
-    float* dst = L.partials + ((size_t)T.part_base + (size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
+    float* dst = T.partials + ((size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
         __hip_atomic_store(dst + t * kTileRows + lane, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -437,7 +456,7 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L
 template <int NTOK>
 __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int tile, int count) {
     const int lane = threadIdx.x;
-    uint32_t* ctr = L.counters + T.tile_base + tile;
+    uint32_t* ctr = T.counters + tile;
     uint32_t old = 0;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
@@ -446,15 +465,31 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
     old = __builtin_amdgcn_readfirstlane(old);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (old + (uint32_t)count != (uint32_t)T.nseg) return;
-    const float* src = L.partials + ((size_t)T.part_base + (size_t)tile * T.nseg) * (NTOK * kTileRows);
+    const float* src = T.partials + (size_t)tile * T.nseg * (NTOK * kTileRows) + lane;
     float sum[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
-    for (int p = 0; p < T.nseg; ++p) {
+    // Batches of kFixBatch segment sums are requested together (indices past
+    // the last segment re-read the last one and are not added), then added
+    // in segment order.
+    constexpr int kFixBatch = 8;
+    for (int p0 = 0; p0 < T.nseg; p0 += kFixBatch) {
+        float v[kFixBatch][NTOK];
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t)
-            sum[t] += __hip_atomic_load(src + ((size_t)p * NTOK + t) * kTileRows + lane, __ATOMIC_RELAXED,
-                                        __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 0; k < kFixBatch; ++k) {
+            const int p = min(p0 + k, T.nseg - 1);
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t)
+                v[k][t] = __hip_atomic_load(src + ((size_t)p * NTOK + t) * kTileRows, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int k = 0; k < kFixBatch; ++k) {
+            if (p0 + k < T.nseg) {
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) sum[t] += v[k][t];
+            }
+        }
     }
     write_rows<NTOK>(T, tile, sum);
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -521,8 +556,8 @@ template <class Col, int NTOK, int DEPTH>
 __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int64_t j0, int64_t j1,
                                              uint8_t* slot) {
     const int S = T.seg, nseg = T.nseg, nb = T.nb;
-    int tile = (int)(j0 / nseg);
-    int seg = (int)(j0 - (int64_t)tile * nseg);
+    int tile = (int)j0 / nseg;            // segment counts fit in int32 (checked on the host)
+    int seg = (int)j0 - tile * nseg;
     int b = seg * S;
     typename Col::Offsets offs;
     offs.init(T);
@@ -561,17 +596,38 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_slot[];
     uint8_t* slot = reinterpret_cast<uint8_t*>(kq_slot);
     const int w = xcd_remap(blockIdx.x, gridDim.x);
-    const int64_t c0 = L.total_cost * w / L.grid;
-    const int64_t c1 = L.total_cost * (w + 1) / L.grid;
+    // the head, in one batch of scalar loads
+    const u32x8* hp = reinterpret_cast<const u32x8*>(&L.h);
+    const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2], g3 = hp[3], g4 = hp[4];
+    asm volatile("" : : "s"(g0), "s"(g1), "s"(g2), "s"(g3), "s"(g4));
+    const int64_t cost_q = (int64_t)(((uint64_t)g0[1] << 32) | g0[0]);
+    const int cost_r = (int)g0[2], n = (int)g0[3];
+    const int64_t c0 = (int64_t)w * cost_q + min(w, cost_r);
+    const int64_t c1 = (int64_t)(w + 1) * cost_q + min(w + 1, cost_r);
+    // first tensor that ends after c0: count the tensors ending at or before
+    // it (the ends are non-decreasing; unused entries are INT64_MAX)
+    int first = 0;
+    const u32x8 ge[4] = {g1, g2, g3, g4};
+#pragma unroll
+    for (int k = 0; k < kMaxSet; ++k) {
+        const u32x8& g = ge[k / 4];
+        const int64_t end = (int64_t)(((uint64_t)g[2 * (k % 4) + 1] << 32) | g[2 * (k % 4)]);
+        first += end <= c0 ? 1 : 0;
+    }
 #pragma unroll 1
-    for (int i = 0; i < L.n; ++i) {
-        const KqDesc T = L.t[i];          // one batch of scalar loads, then registers
+    for (int i = first; i < n; ++i) {
+        const KqDesc T = load_uniform(L.t[i]);
+        if (T.cost_base >= c1) break;     // this and the later tensors are past the range
         const int64_t nsegs = (int64_t)T.tiles * T.nseg;
-        // first segment whose start cost cost_base + j*seg_cost is >= c
+        // first segment whose start cost cost_base + j*seg_cost is >= c: the
+        // quotient from the reciprocal is within one of the exact ceiling
+        // (rel < 2^53), and is then corrected exactly
         auto first_at = [&](int64_t c) -> int64_t {
             const int64_t rel = c - T.cost_base;
             if (rel <= 0) return 0;
-            const int64_t j = (rel + T.seg_cost - 1) / T.seg_cost;
+            int64_t j = (int64_t)((double)rel * T.inv_seg_cost);
+            if (j * T.seg_cost < rel) ++j;
+            else if ((j - 1) * T.seg_cost >= rel) --j;
             return j < nsegs ? j : nsegs;
         };
         const int64_t j0 = first_at(c0), j1 = first_at(c1);
@@ -769,6 +825,8 @@ static int launch_t(KqLaunch L, hipStream_t stream) {
     if (grid > L.total_segments) grid = L.total_segments;
     if (grid < 1) grid = 1;
     L.grid = grid;
+    L.h.cost_q = L.total_cost / grid;
+    L.h.cost_r = (int32_t)(L.total_cost % grid);
     hipLaunchKernelGGL(kq_matvec_kernel<NTOK>, dim3(grid), dim3(64), (size_t)L.lds_bytes, stream, L);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }

@@ -11,10 +11,10 @@
 // same result alone or in a set, and whatever workgroup does the work.
 //
 // The launch is a persistent grid of P one-wave workgroups (about one full
-// round of resident waves).  Workgroup w streams the contiguous run of
-// segments whose starting byte falls in [w*B/P, (w+1)*B/P) of the launch's
-// B weight bytes, prefetching one super-block column ahead across segment
-// and tile boundaries.  A tile whose segments all belong to one workgroup is
+// round of resident waves).  With B = q*P + r weight bytes in the launch,
+// workgroup w streams the contiguous run of segments whose starting byte
+// falls in [c(w), c(w+1)), c(w) = w*q + min(w, r), prefetching ahead across
+// segment and tile boundaries.  A tile whose segments all belong to one workgroup is
 // summed in registers and written directly; a tile shared by workgroups has
 // its segment sums written to a per-stream workspace, and the last
 // contributor (an arrival counter per tile) adds them in order.
@@ -43,7 +43,9 @@ struct KqDesc {
     int64_t ldx, ldy;
     int64_t row_bytes;
     int64_t cost_base;  // weight bytes of the launch before this tensor (segment units)
+    int64_t cost_end;   // cost_base + this tensor's segments * seg_cost
     int64_t seg_cost;   // bytes of one full segment: 64 * S * block_bytes
+    double inv_seg_cost;  // 1 / seg_cost, for a division-free segment search
     int32_t rows;
     int32_t nb;         // super-blocks per row
     int32_t fmt;
@@ -52,19 +54,31 @@ struct KqDesc {
     int32_t seg;        // S: super-blocks per segment (the last one of a row may be shorter)
     int32_t part_base;  // first partial-sum slot (one per segment) in the workspace
     int32_t tile_base;  // first counter in the workspace
+    float* partials;    // this tensor's partial sums in the workspace: [segments][ntok][64]
+    uint32_t* counters; // this tensor's arrival counters: one per tile, zero between calls
 };
+static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
+
+// Read by every workgroup before anything else (in one batch).
+struct KqHead {
+    int64_t cost_q;       // workgroup w starts at cost w * cost_q + min(w, cost_r):
+    int32_t cost_r;       //   total_cost = grid * cost_q + cost_r
+    int32_t n;
+    int64_t reserved[2];
+    int64_t cost_end[kMaxSet];  // t[i].cost_end; INT64_MAX past the last tensor
+};
+static_assert(sizeof(KqHead) == 160, "head is five 32-byte groups");
 
 struct KqLaunch {
+    KqHead h;
     KqDesc t[kMaxSet];
-    float* partials;      // workspace: [segments][ntok][64]
-    uint32_t* counters;   // workspace: one per tile, zero between calls
+    float* partials;      // workspace base: [segments][ntok][64]
+    uint32_t* counters;   // workspace base: one per tile
     int64_t total_cost;   // sum of seg_cost * segments over the set
-    int32_t n;
     int32_t ntok;
     int32_t grid;         // persistent workgroups
     int32_t lds_bytes;
     int32_t total_segments;
-    int32_t pad;
 };
 
 struct KqPlanSizes {
