@@ -40,6 +40,11 @@ typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;   // global (not flat) byte pointer
 
 __device__ __forceinline__ gbytes_t gbytes(const void* p) { return (gbytes_t)(p); }
+// Global (not flat) float pointer: flat accesses would also count against
+// the LDS counter and complete out of order with global loads, which makes
+// the compiler wait for every load in flight after them.
+typedef __attribute__((address_space(1))) float* gfloat_t;
+__device__ __forceinline__ gfloat_t gfloat(float* p) { return (gfloat_t)(p); }
 
 constexpr float kTwo24 = 16777216.0f;        // undoes the 2^-24 of a subnormal code
 
@@ -125,6 +130,18 @@ struct XStage {
 
 __device__ __forceinline__ float4 xread(const uint8_t* xslot, int t, int e) {
     return *reinterpret_cast<const float4*>(xslot + 1024 * t + 4 * e);
+}
+
+// End of one step of a block's multiply-adds: the step's accumulators are
+// complete here and no LDS read of a later step moves above this point.
+// With the x of the next step requested at the top of a step, this keeps two
+// steps of x in registers instead of every read of a Q6_K quarter run
+// hoisted to its start.
+template <int N>
+__device__ __forceinline__ void step_end(float (&a)[N], float (&b)[N]) {
+#pragma unroll
+    for (int t = 0; t < N; ++t) asm volatile("" : "+v"(a[t]), "+v"(b[t]));
+    asm volatile("" : : : "memory");
 }
 
 // ------------------------------------------------------------ Q4_K / Q5_K
@@ -218,14 +235,17 @@ struct K45Column {
     // its last tile) are clamped to the last chunk of its last row, which
     // every such chunk exceeds, so they read valid memory whose values are
     // never used.
-    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b) {
+    // `valid` false: the column lies past the run; every lane then reads the
+    // tensor's first 16 bytes (values unused), so that the loads and the
+    // registers they fill are the same on every path.
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
         const int rows_here = min(kTileRows, T.rows - tile * kTileRows);
-        const uint32_t max_off = (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C - 1);
-        gbytes_t col = gbytes(T.w) + (size_t)tile * kTileRows * T.row_bytes + (size_t)b * BB;
+        const uint32_t max_off = valid ? (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C - 1) : 0u;
+        gbytes_t col = gbytes(T.w) + (valid ? (size_t)tile * kTileRows * T.row_bytes + (size_t)b * BB : (size_t)0);
 #pragma unroll
         for (int i = 0; i < C; ++i)
             stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
-        xs.load(T, b);
+        xs.load(T, valid ? b : 0);
     }
     __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
         const int lane = threadIdx.x;
@@ -303,20 +323,54 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     for (int c = 0; c < 4; ++c)
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) a[c][t] = 0.0f;
+    if constexpr (NTOK <= 2) {
+        // x of step kk (elements 128N + 32c + 4k, c = 0..3) sits in buffer
+        // kk % 2, requested one step ahead
+        float4 xb[2][4][NTOK];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int k = 4 * KH + kk;
-        const Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+        for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int e = 128 * N + 32 * c + 4 * k;
+            for (int t = 0; t < NTOK; ++t) xb[0][c][t] = xread(xslot, t, 128 * N + 32 * c + 4 * (4 * KH));
 #pragma unroll
-            for (int t = 0; t < NTOK; ++t) {
-                const float4 xv = xread(xslot, t, e);
-                a[c][t] = __builtin_fmaf((float)half_lo(p.c02[c]), xv.x, a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_lo(p.c13[c]), xv.y, a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_hi(p.c02[c]), xv.z, a[c][t]);
-                a[c][t] = __builtin_fmaf((float)half_hi(p.c13[c]), xv.w, a[c][t]);
+        for (int kk = 0; kk < 4; ++kk) {
+            const int k = 4 * KH + kk;
+            if (kk + 1 < 4) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int t = 0; t < NTOK; ++t) xb[(kk + 1) % 2][c][t] = xread(xslot, t, 128 * N + 32 * c + 4 * (k + 1));
+            }
+            const Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) {
+                    const float4 xv = xb[kk % 2][c][t];
+                    a[c][t] = __builtin_fmaf((float)half_lo(p.c02[c]), xv.x, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_lo(p.c13[c]), xv.y, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_hi(p.c02[c]), xv.z, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_hi(p.c13[c]), xv.w, a[c][t]);
+                }
+            }
+            step_end<NTOK>(a[0], a[1]);
+            step_end<NTOK>(a[2], a[3]);
+        }
+    } else {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int k = 4 * KH + kk;
+            const Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int e = 128 * N + 32 * c + 4 * k;
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) {
+                    const float4 xv = xread(xslot, t, e);
+                    a[c][t] = __builtin_fmaf((float)half_lo(p.c02[c]), xv.x, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_lo(p.c13[c]), xv.y, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_hi(p.c02[c]), xv.z, a[c][t]);
+                    a[c][t] = __builtin_fmaf((float)half_hi(p.c13[c]), xv.w, a[c][t]);
+                }
             }
         }
     }
@@ -335,31 +389,19 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     }
 }
 
-// Row r of the column: the 53 aligned words from the block's start rounded
-// down to 4 bytes (one load instruction per row, lanes 0..52, addresses
-// uniform).  The tensor's very last block, when it starts 4-byte aligned,
-// ends 2 bytes into its 53rd word; that word is then read as 2 bytes.
-template <bool TAIL>
-__device__ __forceinline__ void q6_stage_rows(uint32_t (&stg)[kTileRows], gbytes_t gw, int64_t start,
-                                              int64_t row_bytes, int rows_here, uint32_t lane4) {
-    const bool word_lane = lane4 < 4 * kQ6Words;
-#pragma unroll
-    for (int r = 0; r < kTileRows; ++r) {
-        if (r < rows_here) {                          // uniform: rows past the tensor's end are skipped
-            gbytes_t rowp = gw + (start & ~(int64_t)3);
-            const __attribute__((address_space(1))) uint32_t* p =
-                (const __attribute__((address_space(1))) uint32_t*)(rowp + lane4);
-            if (!TAIL || r != rows_here - 1) {
-                if (word_lane) stg[r] = *p;
-            } else {
-                if (lane4 < 4 * (kQ6Words - 1)) stg[r] = *p;
-                else if (lane4 == 4 * (kQ6Words - 1)) stg[r] = *(const __attribute__((address_space(1))) uint16_t*)p;
-            }
-        }
-        start += row_bytes;
-    }
-}
-
+// Row r of the column: one load instruction per row, lane i loading word
+// min(i, 52) of the 53 aligned words from the block's start rounded down to
+// 4 bytes (lanes past 52 repeat word 52 and are not written to LDS; rows
+// past the tensor's end repeat row 0).  The rounded-down row starts are
+// offsets from the column's first one: with an even number of blocks a row
+// (row_bytes a multiple of 4) every row has the same alignment; with an odd
+// number the alignment alternates, so odd rows move by 2 bytes the other
+// way.  A row then costs a few scalar operations, two vector ones and the
+// load.  Branch-free, so the register sets of the columns in flight stay
+// simple.  The tensor's very last block, when it starts 4-byte aligned,
+// ends 2 bytes into its 53rd word: in that row the lanes stop at word 51,
+// and bytes 208-209 are read as 2 bytes on their own and written to LDS
+// with the column.
 struct Q6Offsets {
     __device__ __forceinline__ void init(const KqDesc& T) { (void)T; }
 };
@@ -370,19 +412,43 @@ struct Q6Column {
     static constexpr int WSLOT = kTileRows * kQ6LdsRow;
     typedef Q6Offsets Offsets;
     uint32_t stg[kTileRows];
+    uint32_t tailv;       // bytes 208-209 of the tensor's last block (tail case)
+    int tail_row;         // its row in the tile, or -1
     XStage<NTOK> xs;
 
-    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b) {
+    // `valid` false: the column lies past the run; every row then reads
+    // words 0..51 of the tensor's first block (values unused).
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
         (void)o;
         const int r0 = tile * kTileRows;
         const int rows_here = min(kTileRows, T.rows - r0);
-        const uint32_t lane4 = 4u * threadIdx.x;
-        const int64_t start = (int64_t)r0 * T.row_bytes + 210 * (int64_t)b;
-        const int64_t last = (int64_t)(r0 + rows_here - 1) * T.row_bytes + 210 * (int64_t)b;
-        const bool tail = (r0 + rows_here == T.rows) && (b == T.nb - 1) && ((last & 3) == 0);
-        if (!tail) q6_stage_rows<false>(stg, gbytes(T.w), start, T.row_bytes, rows_here, lane4);
-        else q6_stage_rows<true>(stg, gbytes(T.w), start, T.row_bytes, rows_here, lane4);
-        xs.load(T, b);
+        const uint32_t lane = threadIdx.x;
+        const int64_t start = (int64_t)r0 * T.row_bytes + 210 * (int64_t)b;      // row r0's block
+        const int64_t last = start + (int64_t)(rows_here - 1) * T.row_bytes;      // the tile's last row's block
+        const bool tail = valid && (r0 + rows_here == T.rows) && (b == T.nb - 1) && ((last & 3) == 0);
+        const int stop = valid ? rows_here - 1 : 0;                               // last row read
+        const int lw_row = tail ? stop : (valid ? kTileRows : 0);                 // row where lanes stop at 51
+        const uint32_t vo52 = 4u * min(lane, 52u), vo51 = 4u * min(lane, 51u);
+        gbytes_t col = gbytes(T.w) + (valid ? (start & ~(int64_t)3) : 0);
+        // row r's rounded-down start minus row 0's: the step from an even row
+        // to the next odd one is row_bytes + corr, from odd to even
+        // row_bytes - corr (corr = 0 when row_bytes is a multiple of 4)
+        const int32_t a0 = (int32_t)(start & 3), rb = (int32_t)T.row_bytes;
+        const int32_t corr = (rb & 3) ? 2 * a0 - 2 : 0;
+        int32_t roff = 0;
+#pragma unroll
+        for (int r = 0; r < kTileRows; ++r) {
+            if (r > 0) roff += (r & 1) ? rb + corr : rb - corr;
+            const uint32_t ro = r <= stop ? (uint32_t)roff : 0u;               // uniform
+            const uint32_t vo = r >= lw_row ? vo51 : vo52;
+            stg[r] = *(const __attribute__((address_space(1))) uint32_t*)(col + (vo + ro));
+        }
+        tail_row = -1;
+        if (tail) {
+            tail_row = stop;
+            tailv = *(const __attribute__((address_space(1))) uint16_t*)(gbytes(T.w) + last + 208);
+        }
+        xs.load(T, valid ? b : 0);
     }
     __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
         const int lane = threadIdx.x;
@@ -390,6 +456,8 @@ struct Q6Column {
 #pragma unroll
             for (int r = 0; r < kTileRows; ++r) reinterpret_cast<uint32_t*>(slot + r * kQ6LdsRow)[lane] = stg[r];
         }
+        if (tail_row >= 0 && lane == 0)
+            reinterpret_cast<uint32_t*>(slot + tail_row * kQ6LdsRow)[kQ6Words - 1] = tailv;
         xs.template commit<16>(slot + WSLOT, sx);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
@@ -430,7 +498,7 @@ __device__ __forceinline__ void write_rows(const KqDesc& T, int tile, const floa
     const int r0 = tile * kTileRows;
     if (lane < T.rows - r0) {
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t) T.y[t * T.ldy + r0 + lane] = v[t];
+        for (int t = 0; t < NTOK; ++t) gfloat(T.y)[t * T.ldy + r0 + lane] = v[t];
     }
 }
 
@@ -442,7 +510,7 @@ template <int NTOK>
 __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L, int tile, int seg,
                                               const float (&v)[NTOK]) {
     const int lane = threadIdx.x;
-    float* dst = T.partials + ((size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
+    gfloat_t dst = gfloat(T.partials) + ((size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
         __hip_atomic_store(dst + t * kTileRows + lane, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -456,7 +524,7 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L
 template <int NTOK>
 __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int tile, int count) {
     const int lane = threadIdx.x;
-    uint32_t* ctr = T.counters + tile;
+    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + tile);
     uint32_t old = 0;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
@@ -465,7 +533,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
     old = __builtin_amdgcn_readfirstlane(old);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (old + (uint32_t)count != (uint32_t)T.nseg) return;
-    const float* src = T.partials + (size_t)tile * T.nseg * (NTOK * kTileRows) + lane;
+    gfloat_t src = gfloat(T.partials) + (size_t)tile * T.nseg * (NTOK * kTileRows) + lane;
     float sum[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
@@ -497,34 +565,41 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
 
 // ------------------------------------------------------------ a run of segments
 // Segments j0..j1-1 of tensor T (tile-major), one super-block column at a
-// time.  DEPTH columns are in flight: the loads of column i+DEPTH are issued
-// right after column i has been written to LDS, so a workgroup's first
-// DEPTH columns are requested at once.  (Q4_K/Q5_K use DEPTH 2; a Q6_K
-// column needs 64 staging registers per lane, so it uses DEPTH 1.)  The
-// loop state is kept in plain scalars so that it stays in registers.
+// time.  DEPTH columns are in flight in DEPTH register sets used in turn:
+// the loads of column i+DEPTH go into the set of column i as soon as column
+// i has been written to LDS, so a workgroup's first DEPTH columns are
+// requested at once.  Q4_K and Q5_K use DEPTH 2, Q6_K 1 (36, 44 and 64
+// staging registers a column).
 //
-// One column: write column `c` to LDS, refill its registers with the column
-// DEPTH ahead, compute, then close the segment / tile where they end.
+// The step is written out once per register set (static indices) and every
+// step refills its set unconditionally (a column past the run reads a
+// dummy address): a set whose loads may be in flight is then never merged
+// with another value at a branch join, where the compiler would copy it and
+// wait for the loads.
+//
 // Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0); a column whose
 // segment is >= j1 lies past the end of the run.
-#define KQ_STEP(c)                                                                             \
+#define KQ_INSIDE(t_, b_) ((int64_t)(t_) * nseg + (b_) / S < j1)
+#define KQ_ADVANCE(t_, b_)                              \
+    {                                                   \
+        if ((b_) + 1 == nb) { ++(t_); (b_) = 0; }       \
+        else ++(b_);                                    \
+    }
+#define KQ_STEP(k_)                                                                            \
     {                                                                                          \
         __syncthreads();                                /* earlier reads of the slot done */   \
         float sx[NTOK];                                                                        \
-        (c).commit(slot, sx);                                                                  \
+        c[k_].commit(slot, sx);                                                                \
+        {                                                                                      \
+            const bool valid = KQ_INSIDE(itile, ib);                                           \
+            c[k_].stage(T, offs, itile, ib, valid);                                            \
+            if (valid) KQ_ADVANCE(itile, ib)                                                   \
+        }                                                                                      \
         const bool row_end = b + 1 == nb;                                                      \
         const bool seg_end = row_end || (b + 1) % S == 0;                                      \
         const int ntile = row_end ? tile + 1 : tile;                                           \
         const int nbb = row_end ? 0 : b + 1;                                                   \
-        const bool has_next = (int64_t)ntile * nseg + nbb / S < j1;                            \
-        if (DEPTH == 1) {                                                                      \
-            if (has_next) (c).stage(T, offs, ntile, nbb);                                      \
-        } else {                                                                               \
-            const bool nrow_end = nbb + 1 == nb;                                               \
-            const int n2tile = nrow_end ? ntile + 1 : ntile;                                   \
-            const int n2b = nrow_end ? 0 : nbb + 1;                                            \
-            if (has_next && (int64_t)n2tile * nseg + n2b / S < j1) (c).stage(T, offs, n2tile, n2b); \
-        }                                                                                      \
+        const bool has_next = KQ_INSIDE(ntile, nbb);                                           \
         __syncthreads();                                /* slot written */                     \
         Col::compute(T, slot, tile, b, sx, acc);                                               \
         if (seg_end) {                                                                         \
@@ -555,6 +630,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
 template <class Col, int NTOK, int DEPTH>
 __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int64_t j0, int64_t j1,
                                              uint8_t* slot) {
+    static_assert(DEPTH >= 1 && DEPTH <= 3, "1..3 register sets");
     const int S = T.seg, nseg = T.nseg, nb = T.nb;
     int tile = (int)j0 / nseg;            // segment counts fit in int32 (checked on the host)
     int seg = (int)j0 - tile * nseg;
@@ -566,29 +642,40 @@ __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L,
     for (int t = 0; t < NTOK; ++t) { acc[t] = 0.0f; tsum[t] = 0.0f; }
     int pending = 0;
     bool owned = (int64_t)tile * nseg >= j0 && (int64_t)(tile + 1) * nseg <= j1;
-    Col c0;
-    c0.stage(T, offs, tile, b);
-    if constexpr (DEPTH == 2) {
-        Col c1;
-        {
-            const bool row_end = b + 1 == nb;
-            const int ntile = row_end ? tile + 1 : tile;
-            const int nbb = row_end ? 0 : b + 1;
-            if ((int64_t)ntile * nseg + nbb / S < j1) c1.stage(T, offs, ntile, nbb);
-        }
-        while (true) {
-            KQ_STEP(c0)
-            KQ_STEP(c1)
-        }
-    } else {
-        while (true) {
-            KQ_STEP(c0)
-        }
+    Col c[DEPTH];
+    int itile = tile, ib = b;             // the next column to request
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+        const bool valid = KQ_INSIDE(itile, ib);
+        c[d].stage(T, offs, itile, ib, valid);
+        if (valid) KQ_ADVANCE(itile, ib)
+    }
+#pragma unroll 1
+    while (true) {
+        KQ_STEP(0)
+        if constexpr (DEPTH > 1) KQ_STEP(1)
+        if constexpr (DEPTH > 2) KQ_STEP(2)
     }
 }
 #undef KQ_STEP
+#undef KQ_ADVANCE
+#undef KQ_INSIDE
 
 // ------------------------------------------------------------ the kernel
+#ifndef KQ_DEPTH_Q4
+#define KQ_DEPTH_Q4 2
+#endif
+#ifndef KQ_DEPTH_Q5
+#define KQ_DEPTH_Q5 2
+#endif
+#ifndef KQ_DEPTH_Q6
+#define KQ_DEPTH_Q6 1
+#endif
+constexpr int kDepthQ4 = KQ_DEPTH_Q4, kDepthQ5 = KQ_DEPTH_Q5;
+// (two Q6_K columns in flight fit the register file only for one token
+// plane, and measured no faster than one)
+template <int NTOK> constexpr int kDepthQ6 = NTOK == 1 ? KQ_DEPTH_Q6 : 1;
+
 // Persistent grid: workgroup w owns the segments whose first weight byte
 // lies in [w*B/P, (w+1)*B/P) of the launch (B bytes, P workgroups).
 template <int NTOK>
@@ -633,9 +720,9 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
         const int64_t j0 = first_at(c0), j1 = first_at(c1);
         if (j0 >= j1) continue;
         switch (T.fmt) {
-        case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, 2>(T, L, j0, j1, slot); break;
-        case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, 2>(T, L, j0, j1, slot); break;
-        default: run_segments<Q6Column<NTOK>, NTOK, 1>(T, L, j0, j1, slot); break;
+        case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;
+        case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, L, j0, j1, slot); break;
+        default: run_segments<Q6Column<NTOK>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot); break;
         }
     }
 }
