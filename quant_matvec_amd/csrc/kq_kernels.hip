@@ -275,11 +275,8 @@ struct K45Column {
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) { ts_e[t] = 0.0f; ts_o[t] = 0.0f; tm[t] = 0.0f; }
         k45_group<FMT, NTOK, 0>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        __builtin_amdgcn_sched_barrier(0);
         k45_group<FMT, NTOK, 1>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        __builtin_amdgcn_sched_barrier(0);
         k45_group<FMT, NTOK, 2>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        __builtin_amdgcn_sched_barrier(0);
         k45_group<FMT, NTOK, 3>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
         const float d24 = d * kTwo24;
 #pragma unroll
@@ -477,11 +474,8 @@ struct Q6Column {
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
         q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, sx, tl, th);
-        __builtin_amdgcn_sched_barrier(0);
         q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, sx, tl, th);
-        __builtin_amdgcn_sched_barrier(0);
         q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, sx, tl, th);
-        __builtin_amdgcn_sched_barrier(0);
         q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, sx, tl, th);
         const float d24 = d * kTwo24;
 #pragma unroll
