@@ -150,27 +150,21 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, synchronized on both sides
+    # ---- timed region: K steps, synchronized on both sides. HIP events on the
+    # launch stream bracket the same region; with the launches back to back,
+    # their span over all launches is the kernel's average launch duration
+    # (per-launch event pairs would add their own queue time to a ~20 us kernel).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for _ in range(args.steps):
         step()
+    ev1.record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-
-    # ---- kernel durations: HIP events around every launch on the launch stream
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_launch)]
-    reps = max(1, min(args.steps, 10))
-    durs = []
-    torch.cuda.synchronize()
-    for _ in range(reps):
-        for s, (a, b) in zip(sets, ev):
-            a.record(stream)
-            kq.kq_matvec_set(s, ntok=ntok, stream=sptr)
-            b.record(stream)
-        torch.cuda.synchronize()
-        durs.extend(a.elapsed_time(b) * 1e3 for a, b in ev)   # microseconds
-    avg_launch_us = float(np.mean(durs))
+    avg_launch_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * n_launch)
     bytes_per_launch = algo_bytes / n_launch
     achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
 

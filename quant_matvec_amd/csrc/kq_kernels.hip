@@ -4,24 +4,25 @@
 // never stored (muser-book Ch 13 "The QKV + gate matvec family", section
 // 13.1; formats from muser-book Ch 6 sections 6.2-6.4).
 //
-// Mapping (one wave64 per workgroup, see kq_plan.h for the items):
+// Mapping (one wave64 per workgroup, see kq_plan.h for the work items):
 //   * lane i owns output row r0+i, so all 64 lanes walk the same super-block
 //     column at the same time.  The x values a multiply-add needs are then
-//     the same for the whole wave: they are read with scalar loads into
-//     SGPRs and used directly as an operand of v_fma_mix_f32, costing no
-//     VGPRs, no LDS bandwidth and no per-lane memory traffic.
+//     the same for the whole wave: the column's x (1 KB per token plane)
+//     is written to LDS next to the weights and read back with
+//     wave-uniform addresses (LDS broadcast reads).
 //   * The 64 rows of a super-block column are strided in HBM (one row every
-//     row_bytes).  They are fetched with coalesced 16-byte loads (4-byte
-//     loads for the 210-byte Q6_K blocks) into registers, written to a
-//     per-wave LDS slot, and read back one row per lane: a transpose through
-//     LDS.  The next column's loads are issued before the current column is
-//     computed, so one column is always in flight per wave.
+//     row_bytes).  They are fetched with coalesced 16-byte loads (one 4-byte
+//     load per row and lane for the 210-byte Q6_K blocks) into registers,
+//     written to a per-wave LDS slot, and read back one row per lane: a
+//     transpose through LDS.  The loads of the next columns are issued before
+//     the current column is computed (two columns in flight for Q4_K and
+//     Q5_K, one for Q6_K).
 //   * Codes become binary16 subnormals two per word (kq_decode.h) and feed
 //     v_fma_mix_f32 directly: one instruction per weight for the
 //     multiply-add, plus about 0.6 (Q4_K) to 1.4 (Q6_K) bit operations per
 //     weight to unpack.
 //   * Scales are applied once per sub-block (deferred scaling, muser-book
-//     Ch 13 section 13.4.2): per sub-block j the lane accumulates
+//     Ch 13 section 13.4): per sub-block j the lane accumulates
 //     sum(q*x) and adds d*sc_j*that - dmin*m_j*sum(x); sum(x) over each
 //     sub-block is computed once per column by the wave with DPP reductions.
 //   * No MFMA: at ntok <= 8 this is a streaming dot product, not a dense
@@ -34,7 +35,6 @@
 
 namespace kq {
 
-typedef const float __attribute__((address_space(4)))* xconst_t;   // scalar-loadable view of x
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 typedef const __attribute__((address_space(1))) uint8_t* gbytes_t;   // global (not flat) byte pointer
