@@ -58,8 +58,8 @@ def measured_traffic(wname):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="stream52",
                    choices=["stream52", "qkvg_set", "lm_head", "single_q4k", "kv_pair"])
     p.add_argument("--ntok", type=int, default=1, help="kv_pair only")

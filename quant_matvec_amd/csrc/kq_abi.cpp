@@ -32,15 +32,16 @@ static int32_t slot_bytes(int32_t fmt, int32_t ntok) {
     return (fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K : kSlotBytesQ6K) + 1024 * ntok;
 }
 
-// Segment length of one tensor: 2 super-blocks (18-27 KB per 64-row
-// segment), so even a single attention set yields enough segments for a
-// full round of workgroups, while a large matrix needs few partial sums.
+// Segment length S: 2 super-blocks (18-27 KB per 64-row segment), except
+// for Q6_K matrices of at most kSmallRows rows, which take 1 (13 KB).  A
+// decode set then splits into runs of similar size (its small Q6_K K and V
+// would otherwise be the longest runs), while a large matrix keeps few
+// partial sums.  Depends on (fmt, rows, cols) only.
+constexpr int64_t kSmallRows = 16384;
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg) {
-    (void)fmt;
-    (void)rows;
     const int64_t nb = cols / 256;
-    const int64_t S = nb < 2 ? nb : 2;
-    *seg = (int32_t)S;
+    const int32_t S = (fmt == KQ_Q6_K && rows <= kSmallRows) ? 1 : 2;
+    *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
 }
 
@@ -100,9 +101,8 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
 int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPlanSizes* sz) {
     *L = KqLaunch{};
     L->h.n = n;
-    for (int i = 0; i < kMaxSet; ++i) L->h.cost_end[i] = INT64_MAX;
+    for (int i = 0; i < kMaxSet; ++i) L->h.wg_end[i] = INT32_MAX;
     L->ntok = ntok;
-    int64_t cost = 0;
     int32_t parts = 0, tiles = 0, lds = 0, segs = 0;
     for (int i = 0; i < n; ++i) {
         const kq_tensor& T = t[i];
@@ -118,12 +118,6 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.fmt = T.fmt;
         D.tiles = (int32_t)((T.rows + kTileRows - 1) / kTileRows);
         plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg);
-        D.seg_cost = (int64_t)kTileRows * D.seg * block_bytes(T.fmt);
-        D.inv_seg_cost = 1.0 / (double)D.seg_cost;
-        D.cost_base = cost;
-        cost += (int64_t)D.tiles * D.nseg * D.seg_cost;
-        D.cost_end = cost;
-        L->h.cost_end[i] = cost;
         D.part_base = parts;
         parts += D.tiles * D.nseg;
         D.tile_base = tiles;
@@ -131,12 +125,73 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         segs += D.tiles * D.nseg;
         if (slot_bytes(T.fmt, ntok) > lds) lds = slot_bytes(T.fmt, ntok);
     }
-    L->total_cost = cost;
     L->total_segments = segs;
     L->lds_bytes = lds;
     sz->partial_floats = (size_t)parts * ntok * kTileRows;
     sz->counters = (size_t)tiles;
     return KQ_OK;
+}
+
+// Workgroups of the tensors for a bound C on the bytes of one workgroup's
+// run: every tensor's runs hold max(1, C / segment bytes) segments.
+static int64_t workgroups_for(const KqLaunch& L, int64_t C, int32_t* per_wg) {
+    int64_t P = 0;
+    for (int i = 0; i < L.h.n; ++i) {
+        const KqDesc& D = L.t[i];
+        const int64_t segs = (int64_t)D.tiles * D.nseg;
+        const int64_t seg_bytes = (int64_t)kTileRows * (D.nb < D.seg ? D.nb : D.seg) * block_bytes(D.fmt);
+        int64_t k = C / seg_bytes;
+        if (k < 1) k = 1;
+        if (k > segs) k = segs;
+        if (per_wg) per_wg[i] = (int32_t)k;
+        P += (segs + k - 1) / k;
+    }
+    return P;
+}
+
+void assign_workgroups(KqLaunch* L, int32_t capacity) {
+    const int n = L->h.n;
+    if (capacity < n) capacity = n;
+    // smallest C (bytes) whose split fits in `capacity` workgroups: the
+    // workgroup count only falls as C grows, and one workgroup per tensor
+    // (C = the largest tensor) always fits
+    int64_t lo = 0, hi = 0;
+    for (int i = 0; i < n; ++i) {
+        const KqDesc& D = L->t[i];
+        const int64_t bytes = (int64_t)D.tiles * kTileRows * D.row_bytes;
+        if (bytes > hi) hi = bytes;
+    }
+    while (lo < hi) {
+        const int64_t mid = lo + (hi - lo) / 2;
+        if (workgroups_for(*L, mid, nullptr) <= capacity) hi = mid;
+        else lo = mid + 1;
+    }
+    int32_t k[kMaxSet], P[kMaxSet];
+    const int64_t used = workgroups_for(*L, hi, k);
+    // workgroups left over go to the tensors in proportion to their bytes
+    // (more resident waves keep more bytes in flight on a large launch)
+    int64_t total = 0;
+    for (int i = 0; i < n; ++i) total += (int64_t)L->t[i].tiles * kTileRows * L->t[i].row_bytes;
+    const int64_t slack = capacity - used;
+    for (int i = 0; i < n; ++i) {
+        const KqDesc& D = L->t[i];
+        const int32_t segs = D.tiles * D.nseg;
+        const int64_t bytes = (int64_t)D.tiles * kTileRows * D.row_bytes;
+        int64_t p = (segs + k[i] - 1) / k[i] + (total > 0 ? (int64_t)((double)slack * (double)bytes / (double)total) : 0);
+        P[i] = (int32_t)(p < segs ? p : segs);
+    }
+    int32_t base = 0;
+    for (int i = 0; i < n; ++i) {
+        KqDesc& D = L->t[i];
+        const int32_t segs = D.tiles * D.nseg;
+        D.wg_base = base;
+        D.wg_count = P[i];
+        D.seg_q = segs / P[i];
+        D.seg_r = segs % P[i];
+        base += P[i];
+        L->h.wg_end[i] = base;
+    }
+    L->grid = base;
 }
 
 // -------------------------------------------------------------- workspaces

@@ -291,11 +291,12 @@ struct K45Column {
 // -------------------------------------------------------------------- Q6_K
 // 210-byte block: ql[128], qh[64], sc[16] (int8), d (f16, last).  A block
 // starts 2 bytes into a word when its index in the tensor is odd, so each
-// row's block is staged as the 53 aligned words covering it (one row per
-// load instruction, lanes 0..52, all addressing uniform) into a 240-byte
-// LDS row, and shifted by two bytes after the LDS read where needed.
-constexpr int kQ6Words = 53;
-constexpr int kQ6LdsRow = 240;
+// row's block is staged as the 53 aligned words covering it: words 0..51 as
+// 13 16-byte chunks (a column is 13 load instructions of 64 chunks, like
+// the Q4_K/Q5_K path) into a 208-byte LDS row, and word 52 (lane = row) into
+// a separate 64-word array.  The compute shifts by two bytes where needed.
+constexpr int kQ6Chunks = 13;
+constexpr int kQ6LdsRow = 16 * kQ6Chunks;     // 208: 52 words, odd multiple of 4 -> conflict-free rows
 
 // The block's words w[i..i+3] (and w[i+4] for the shift) realigned.
 __device__ __forceinline__ void q6_read4(const uint8_t* row, int i, uint32_t sh, uint32_t (&o)[4]) {
@@ -386,75 +387,87 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     }
 }
 
-// Row r of the column: one load instruction per row, lane i loading word
-// min(i, 52) of the 53 aligned words from the block's start rounded down to
-// 4 bytes (lanes past 52 repeat word 52 and are not written to LDS; rows
-// past the tensor's end repeat row 0).  The rounded-down row starts are
-// offsets from the column's first one: with an even number of blocks a row
-// (row_bytes a multiple of 4) every row has the same alignment; with an odd
-// number the alignment alternates, so odd rows move by 2 bytes the other
-// way.  A row then costs a few scalar operations, two vector ones and the
-// load.  Branch-free, so the register sets of the columns in flight stay
-// simple.  The tensor's very last block, when it starts 4-byte aligned,
-// ends 2 bytes into its 53rd word: in that row the lanes stop at word 51,
-// and bytes 208-209 are read as 2 bytes on their own and written to LDS
-// with the column.
+// Per-lane staging offsets of a 64-row Q6_K column.  Chunk q = 64*i + lane
+// is row q / 13, words 4*(q % 13).. of that row's aligned span; word 52 of
+// row `lane` is one more dword load.  With an even number of blocks per row
+// (row_bytes a multiple of 4) every row of a column has the same alignment.
+// With an odd number (ALT) it alternates between rows: an odd row's aligned
+// start sits 2 bytes away from row_bytes * row, in the direction that row
+// 0's alignment gives (`corr`, set per column); bit i of `odd` marks chunk
+// i's row as odd, bit 13 the lane's own row.
+template <bool ALT>
 struct Q6Offsets {
-    __device__ __forceinline__ void init(const KqDesc& T) { (void)T; }
+    uint32_t off[kQ6Chunks];
+    uint32_t off52;
+    uint32_t odd;
+    __device__ __forceinline__ void init(const KqDesc& T) {
+        int lane = threadIdx.x;
+        asm volatile("" : "+v"(lane));
+        const uint32_t rb = (uint32_t)T.row_bytes;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kQ6Chunks; ++i) {
+            const uint32_t q = 64u * i + (uint32_t)lane;
+            const uint32_t r = q / kQ6Chunks, c = q - r * kQ6Chunks;
+            off[i] = r * rb + 16u * c;
+            m |= (r & 1u) << i;
+        }
+        off52 = (uint32_t)lane * rb + 208u;
+        odd = ALT ? (m | (((uint32_t)lane & 1u) << 13)) : 0u;
+    }
+    // offset of chunk i (13: word 52) for a column whose odd rows move by corr
+    __device__ __forceinline__ uint32_t at(int i, int32_t corr) const {
+        const uint32_t o = i < kQ6Chunks ? off[i] : off52;
+        if constexpr (!ALT) return o;
+        return o + (uint32_t)((int32_t)((odd >> i) & 1u) * corr);
+    }
 };
 
-template <int NTOK>
+template <int NTOK, bool ALT>
 struct Q6Column {
     static constexpr int SUB = 16;
-    static constexpr int WSLOT = kTileRows * kQ6LdsRow;
-    typedef Q6Offsets Offsets;
-    uint32_t stg[kTileRows];
+    static constexpr int WSLOT = kTileRows * kQ6LdsRow + 4 * kTileRows;
+    typedef Q6Offsets<ALT> Offsets;
+    uint4 stg[kQ6Chunks];
+    uint32_t w52;         // word 52 of the lane's row
     uint32_t tailv;       // bytes 208-209 of the tensor's last block (tail case)
     int tail_row;         // its row in the tile, or -1
     XStage<NTOK> xs;
 
-    // `valid` false: the column lies past the run; every row then reads
-    // words 0..51 of the tensor's first block (values unused).
+    // Branch-free.  Chunks of rows past the tensor's end are clamped to the
+    // last chunk of its last row (every such chunk's offset exceeds it).
+    // The tensor's very last block, when it starts 4-byte aligned, ends 2
+    // bytes into its word 52: that row reads its word 51 instead, and bytes
+    // 208-209 are read on their own and put in its place at the commit.
+    // `valid` false: the column lies past the run; every lane then reads the
+    // tensor's first bytes (values unused).
     __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
-        (void)o;
         const int r0 = tile * kTileRows;
-        const int rows_here = min(kTileRows, T.rows - r0);
-        const uint32_t lane = threadIdx.x;
-        const int64_t start = (int64_t)r0 * T.row_bytes + 210 * (int64_t)b;      // row r0's block
-        const int64_t last = start + (int64_t)(rows_here - 1) * T.row_bytes;      // the tile's last row's block
-        const bool tail = valid && (r0 + rows_here == T.rows) && (b == T.nb - 1) && ((last & 3) == 0);
-        const int stop = valid ? rows_here - 1 : 0;                               // last row read
-        const int lw_row = tail ? stop : (valid ? kTileRows : 0);                 // row where lanes stop at 51
-        const uint32_t vo52 = 4u * min(lane, 52u), vo51 = 4u * min(lane, 51u);
+        const int last_row = min(kTileRows, T.rows - r0) - 1;
+        const int32_t rb = (int32_t)T.row_bytes;
+        const int64_t start = (int64_t)r0 * T.row_bytes + 210 * (int64_t)b;    // row r0's block
+        const int64_t last = start + (int64_t)last_row * T.row_bytes;         // the tile's last row's block
+        const bool tail = valid && (r0 + last_row + 1 == T.rows) && (b == T.nb - 1) && ((last & 3) == 0);
+        const int32_t corr = ALT ? 2 * (int32_t)(start & 3) - 2 : 0;
+        const int32_t dl = (last_row & 1) ? corr : 0;
+        uint32_t max_off = valid ? (uint32_t)(last_row * rb + 16 * (kQ6Chunks - 1) + dl) : 0u;
+        uint32_t max52 = valid ? (uint32_t)(last_row * rb + (tail ? 204 : 208) + dl) : 0u;
+        asm volatile("" : "+s"(max_off), "+s"(max52));
         gbytes_t col = gbytes(T.w) + (valid ? (start & ~(int64_t)3) : 0);
-        // row r's rounded-down start minus row 0's: the step from an even row
-        // to the next odd one is row_bytes + corr, from odd to even
-        // row_bytes - corr (corr = 0 when row_bytes is a multiple of 4)
-        const int32_t a0 = (int32_t)(start & 3), rb = (int32_t)T.row_bytes;
-        const int32_t corr = (rb & 3) ? 2 * a0 - 2 : 0;
-        int32_t roff = 0;
 #pragma unroll
-        for (int r = 0; r < kTileRows; ++r) {
-            if (r > 0) roff += (r & 1) ? rb + corr : rb - corr;
-            const uint32_t ro = r <= stop ? (uint32_t)roff : 0u;               // uniform
-            const uint32_t vo = r >= lw_row ? vo51 : vo52;
-            stg[r] = *(const __attribute__((address_space(1))) uint32_t*)(col + (vo + ro));
-        }
-        tail_row = -1;
-        if (tail) {
-            tail_row = stop;
-            tailv = *(const __attribute__((address_space(1))) uint16_t*)(gbytes(T.w) + last + 208);
-        }
+        for (int i = 0; i < kQ6Chunks; ++i)
+            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(
+                                                  col + min(o.at(i, corr), max_off)));
+        w52 = *(const __attribute__((address_space(1))) uint32_t*)(col + min(o.at(kQ6Chunks, corr), max52));
+        tail_row = tail ? last_row : -1;
+        tailv = *(const __attribute__((address_space(1))) uint16_t*)(gbytes(T.w) + (tail ? last + 208 : 0));
         xs.load(T, valid ? b : 0);
     }
     __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
         const int lane = threadIdx.x;
-        if (lane < kQ6Words) {
 #pragma unroll
-            for (int r = 0; r < kTileRows; ++r) reinterpret_cast<uint32_t*>(slot + r * kQ6LdsRow)[lane] = stg[r];
-        }
-        if (tail_row >= 0 && lane == 0)
-            reinterpret_cast<uint32_t*>(slot + tail_row * kQ6LdsRow)[kQ6Words - 1] = tailv;
+        for (int i = 0; i < kQ6Chunks; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
+        reinterpret_cast<uint32_t*>(slot + kTileRows * kQ6LdsRow)[lane] = lane == tail_row ? tailv : w52;
         xs.template commit<16>(slot + WSLOT, sx);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
@@ -464,12 +477,17 @@ struct Q6Column {
         const uint8_t* xslot = slot + WSLOT;
         // the block starts 2 bytes into its first staged word when its index
         // in the tensor, (r0+lane)*nb + b, is odd
-        const uint32_t sh = (T.nb & 1) == 0 ? 16u * (uint32_t)(b & 1)
-                                            : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
+        const uint32_t sh = !ALT ? 16u * (uint32_t)(b & 1)
+                                 : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
+        // words 48..51 (scales) and word 52 (scales 14-15 and d, or d alone)
+        const uint32_t w52 = lds_read1(slot + kTileRows * kQ6LdsRow + 4 * lane);
+        const uint4 s4 = lds_read4(row + 4 * 48);
         uint32_t scw[4];
-        q6_read4(row, 48, sh, scw);
-        const uint32_t dw = __builtin_amdgcn_alignbit(lds_read1(row + 4 * 53), lds_read1(row + 4 * 52), sh);
-        const float d = f16_to_f32(dw & 0xFFFFu);
+        scw[0] = __builtin_amdgcn_alignbit(s4.y, s4.x, sh);
+        scw[1] = __builtin_amdgcn_alignbit(s4.z, s4.y, sh);
+        scw[2] = __builtin_amdgcn_alignbit(s4.w, s4.z, sh);
+        scw[3] = __builtin_amdgcn_alignbit(w52, s4.w, sh);
+        const float d = f16_to_f32((w52 >> sh) & 0xFFFFu);
         float tl[NTOK], th[NTOK];
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
@@ -533,8 +551,8 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
     for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
     // Batches of kFixBatch segment sums are requested together (indices past
     // the last segment re-read the last one and are not added), then added
-    // in segment order.
-    constexpr int kFixBatch = 8;
+    // in segment order: a 26-segment row of one token plane in one batch.
+    constexpr int kFixBatch = NTOK == 1 ? 32 : NTOK == 2 ? 16 : 8;
     for (int p0 = 0; p0 < T.nseg; p0 += kFixBatch) {
         float v[kFixBatch][NTOK];
 #pragma unroll
@@ -571,13 +589,17 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
 // with another value at a branch join, where the compiler would copy it and
 // wait for the loads.
 //
-// Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0); a column whose
-// segment is >= j1 lies past the end of the run.
-#define KQ_INSIDE(t_, b_) ((int64_t)(t_) * nseg + (b_) / S < j1)
-#define KQ_ADVANCE(t_, b_)                              \
-    {                                                   \
-        if ((b_) + 1 == nb) { ++(t_); (b_) = 0; }       \
-        else ++(b_);                                    \
+// Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0), carrying the
+// segment index j = tile*nseg + b/S along (it moves on at a segment's last
+// block or a row's end); a column whose segment is >= j1 lies past the end
+// of the run.  S is 1 or 2, so b is a segment's last block when
+// (b & smask) == smask, smask = S - 1.  All of it is 32-bit scalar
+// arithmetic (segment counts fit in int32).
+#define KQ_LAST_OF_SEG(b_) (((b_) & smask) == smask)
+#define KQ_ADVANCE(t_, b_, j_)                                      \
+    {                                                               \
+        if ((b_) + 1 == nb) { ++(t_); (b_) = 0; ++(j_); }             \
+        else { (j_) += KQ_LAST_OF_SEG(b_) ? 1 : 0; ++(b_); }          \
     }
 #define KQ_STEP(k_)                                                                            \
     {                                                                                          \
@@ -585,15 +607,16 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
         float sx[NTOK];                                                                        \
         c[k_].commit(slot, sx);                                                                \
         {                                                                                      \
-            const bool valid = KQ_INSIDE(itile, ib);                                           \
+            const bool valid = ij < j1;                                                        \
             c[k_].stage(T, offs, itile, ib, valid);                                            \
-            if (valid) KQ_ADVANCE(itile, ib)                                                   \
+            if (valid) KQ_ADVANCE(itile, ib, ij)                                               \
         }                                                                                      \
         const bool row_end = b + 1 == nb;                                                      \
-        const bool seg_end = row_end || (b + 1) % S == 0;                                      \
+        const bool seg_end = row_end || KQ_LAST_OF_SEG(b);                                     \
         const int ntile = row_end ? tile + 1 : tile;                                           \
         const int nbb = row_end ? 0 : b + 1;                                                   \
-        const bool has_next = KQ_INSIDE(ntile, nbb);                                           \
+        const int nj = seg_end ? j + 1 : j;                                                    \
+        const bool has_next = nj < j1;                                                         \
         __syncthreads();                                /* slot written */                     \
         Col::compute(T, slot, tile, b, sx, acc);                                               \
         if (seg_end) {                                                                         \
@@ -616,33 +639,34 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
             seg = row_end ? 0 : seg + 1;                                                       \
         }                                                                                      \
         if (!has_next) break;                                                                  \
-        if (row_end) owned = (int64_t)ntile * nseg >= j0 && (int64_t)(ntile + 1) * nseg <= j1; \
+        if (row_end) owned = nj >= j0 && nj + nseg <= j1;                                      \
         tile = ntile;                                                                          \
         b = nbb;                                                                               \
+        j = nj;                                                                                \
     }
 
 template <class Col, int NTOK, int DEPTH>
-__device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int64_t j0, int64_t j1,
-                                             uint8_t* slot) {
+__device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int j0, int j1, uint8_t* slot) {
     static_assert(DEPTH >= 1 && DEPTH <= 3, "1..3 register sets");
-    const int S = T.seg, nseg = T.nseg, nb = T.nb;
-    int tile = (int)j0 / nseg;            // segment counts fit in int32 (checked on the host)
-    int seg = (int)j0 - tile * nseg;
-    int b = seg * S;
+    const int nseg = T.nseg, nb = T.nb, smask = T.seg - 1;
+    int tile = j0 / nseg;
+    int seg = j0 - tile * nseg;
+    int b = seg * T.seg;
+    int j = j0;
     typename Col::Offsets offs;
     offs.init(T);
     float acc[NTOK], tsum[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) { acc[t] = 0.0f; tsum[t] = 0.0f; }
     int pending = 0;
-    bool owned = (int64_t)tile * nseg >= j0 && (int64_t)(tile + 1) * nseg <= j1;
+    bool owned = seg == 0 && j0 + nseg <= j1;
     Col c[DEPTH];
-    int itile = tile, ib = b;             // the next column to request
+    int itile = tile, ib = b, ij = j;     // the next column to request
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
-        const bool valid = KQ_INSIDE(itile, ib);
+        const bool valid = ij < j1;
         c[d].stage(T, offs, itile, ib, valid);
-        if (valid) KQ_ADVANCE(itile, ib)
+        if (valid) KQ_ADVANCE(itile, ib, ij)
     }
 #pragma unroll 1
     while (true) {
@@ -653,7 +677,7 @@ __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L,
 }
 #undef KQ_STEP
 #undef KQ_ADVANCE
-#undef KQ_INSIDE
+#undef KQ_LAST_OF_SEG
 
 // ------------------------------------------------------------ the kernel
 #ifndef KQ_DEPTH_Q4
@@ -670,8 +694,8 @@ constexpr int kDepthQ4 = KQ_DEPTH_Q4, kDepthQ5 = KQ_DEPTH_Q5;
 // plane, and measured no faster than one)
 template <int NTOK> constexpr int kDepthQ6 = NTOK == 1 ? KQ_DEPTH_Q6 : 1;
 
-// Persistent grid: workgroup w owns the segments whose first weight byte
-// lies in [w*B/P, (w+1)*B/P) of the launch (B bytes, P workgroups).
+// Workgroup w belongs to the tensor i with wg_end[i-1] <= w < wg_end[i] and
+// streams run u = w - wg_base of it: segments [u*seg_q + min(u, seg_r), ...).
 template <int NTOK>
 __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_slot[];
@@ -679,45 +703,26 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     const int w = xcd_remap(blockIdx.x, gridDim.x);
     // the head, in one batch of scalar loads
     const u32x8* hp = reinterpret_cast<const u32x8*>(&L.h);
-    const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2], g3 = hp[3], g4 = hp[4];
-    asm volatile("" : : "s"(g0), "s"(g1), "s"(g2), "s"(g3), "s"(g4));
-    const int64_t cost_q = (int64_t)(((uint64_t)g0[1] << 32) | g0[0]);
-    const int cost_r = (int)g0[2], n = (int)g0[3];
-    const int64_t c0 = (int64_t)w * cost_q + min(w, cost_r);
-    const int64_t c1 = (int64_t)(w + 1) * cost_q + min(w + 1, cost_r);
-    // first tensor that ends after c0: count the tensors ending at or before
-    // it (the ends are non-decreasing; unused entries are INT64_MAX)
-    int first = 0;
-    const u32x8 ge[4] = {g1, g2, g3, g4};
+    const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2];
+    asm volatile("" : : "s"(g0), "s"(g1), "s"(g2));
+    const int n = (int)g0[0];
+    // the tensor: count the tensors ending at or before w (the ends are
+    // increasing; unused entries are INT32_MAX)
+    int i = 0;
 #pragma unroll
-    for (int k = 0; k < kMaxSet; ++k) {
-        const u32x8& g = ge[k / 4];
-        const int64_t end = (int64_t)(((uint64_t)g[2 * (k % 4) + 1] << 32) | g[2 * (k % 4)]);
-        first += end <= c0 ? 1 : 0;
-    }
-#pragma unroll 1
-    for (int i = first; i < n; ++i) {
-        const KqDesc T = load_uniform(L.t[i]);
-        if (T.cost_base >= c1) break;     // this and the later tensors are past the range
-        const int64_t nsegs = (int64_t)T.tiles * T.nseg;
-        // first segment whose start cost cost_base + j*seg_cost is >= c: the
-        // quotient from the reciprocal is within one of the exact ceiling
-        // (rel < 2^53), and is then corrected exactly
-        auto first_at = [&](int64_t c) -> int64_t {
-            const int64_t rel = c - T.cost_base;
-            if (rel <= 0) return 0;
-            int64_t j = (int64_t)((double)rel * T.inv_seg_cost);
-            if (j * T.seg_cost < rel) ++j;
-            else if ((j - 1) * T.seg_cost >= rel) --j;
-            return j < nsegs ? j : nsegs;
-        };
-        const int64_t j0 = first_at(c0), j1 = first_at(c1);
-        if (j0 >= j1) continue;
-        switch (T.fmt) {
-        case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;
-        case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, L, j0, j1, slot); break;
-        default: run_segments<Q6Column<NTOK>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot); break;
-        }
+    for (int k = 0; k < kMaxSet; ++k) i += (int)(k < 8 ? g1[k] : g2[k - 8]) <= w ? 1 : 0;
+    if (i >= n) return;
+    const KqDesc T = load_uniform(L.t[i]);
+    const int u = w - T.wg_base;
+    const int j0 = u * T.seg_q + min(u, T.seg_r);
+    const int j1 = j0 + T.seg_q + (u < T.seg_r ? 1 : 0);
+    switch (T.fmt) {
+    case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;
+    case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, L, j0, j1, slot); break;
+    default:
+        if (T.nb & 1) run_segments<Q6Column<NTOK, true>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot);
+        else run_segments<Q6Column<NTOK, false>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot);
+        break;
     }
 }
 
@@ -870,6 +875,14 @@ __global__ void kq_dequant_kernel(int32_t fmt, const uint8_t* w, int64_t rows, i
 }
 
 // ------------------------------------------------------------ launchers
+// At most two waves per SIMD: more resident waves (the kernel would fit
+// three at one token plane) spread the same bytes over more concurrent row
+// streams and measured slower on large matrices.
+#ifndef KQ_MAX_WAVES_PER_CU
+#define KQ_MAX_WAVES_PER_CU 8
+#endif
+constexpr int kMaxWavesPerCU = KQ_MAX_WAVES_PER_CU;
+
 // Resident one-wave workgroups per compute unit for this kernel and LDS
 // size (queried once per device, token count and LDS size).
 template <int NTOK>
@@ -901,14 +914,9 @@ template <int NTOK>
 static int launch_t(KqLaunch L, hipStream_t stream) {
     const int cus = compute_units();
     if (cus <= 0) return KQ_ERR_HIP;
-    const int per_cu = resident_per_cu<NTOK>(L.lds_bytes);
-    int grid = per_cu * cus;
-    if (grid > L.total_segments) grid = L.total_segments;
-    if (grid < 1) grid = 1;
-    L.grid = grid;
-    L.h.cost_q = L.total_cost / grid;
-    L.h.cost_r = (int32_t)(L.total_cost % grid);
-    hipLaunchKernelGGL(kq_matvec_kernel<NTOK>, dim3(grid), dim3(64), (size_t)L.lds_bytes, stream, L);
+    const int per_cu = min(resident_per_cu<NTOK>(L.lds_bytes), kMaxWavesPerCU);
+    assign_workgroups(&L, per_cu * cus);
+    hipLaunchKernelGGL(kq_matvec_kernel<NTOK>, dim3(L.grid), dim3(64), (size_t)L.lds_bytes, stream, L);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 

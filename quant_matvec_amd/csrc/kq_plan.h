@@ -4,20 +4,23 @@
 //
 // Work decomposition.  Rows are taken 64 at a time (a TILE: one row per
 // lane of a wave64).  Each tile row is cut into SEGMENTS of S consecutive
-// super-blocks; the segments of a tensor are numbered tile-major.  The row
-// results of a tile are the ordered sum ((0 + seg_0) + seg_1) + ... of its
-// segment sums, each segment accumulated block by block.  S depends only on
-// the tensor's own (format, rows, cols), so a tensor computes bitwise the
-// same result alone or in a set, and whatever workgroup does the work.
+// super-blocks (S = 2, or 1 for a Q6_K matrix of at most 16384 rows); the
+// segments of a tensor are numbered tile-major.  The row results of a tile are the ordered sum
+// ((0 + seg_0) + seg_1) + ... of its segment sums, each segment accumulated
+// block by block.  S depends only on the tensor's own shape, so a tensor
+// computes bitwise the same result alone or in a set, and whatever
+// workgroup does the work.
 //
-// The launch is a persistent grid of P one-wave workgroups (about one full
-// round of resident waves).  With B = q*P + r weight bytes in the launch,
-// workgroup w streams the contiguous run of segments whose starting byte
-// falls in [c(w), c(w+1)), c(w) = w*q + min(w, r), prefetching ahead across
-// segment and tile boundaries.  A tile whose segments all belong to one workgroup is
-// summed in registers and written directly; a tile shared by workgroups has
-// its segment sums written to a per-stream workspace, and the last
-// contributor (an arrival counter per tile) adds them in order.
+// The launch is a grid of one-wave workgroups, at most one full round of
+// resident waves, split between the tensors of the set: tensor i gets P_i
+// workgroups, each streaming a contiguous run of its segments (the runs'
+// lengths differ by at most one), prefetching ahead across segment and tile
+// boundaries.  The P_i are chosen so that the largest run, in weight bytes,
+// is as small as the round of resident waves allows.  A tile whose segments
+// all belong to one workgroup is summed in registers and written directly;
+// a tile shared by workgroups has its segment sums written to a per-stream
+// workspace, and the last contributor (an arrival counter per tile) adds
+// them in order.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -30,11 +33,11 @@ constexpr int kTileRows = 64;             // rows per item: one per lane of a wa
 constexpr int kMaxSet = KQ_MAX_SET;
 
 // Bytes one item stages in LDS for one super-block column (64 rows).  Q6_K
-// rows are copied as 53 aligned dwords into a 240-byte LDS row (240/16 odd
-// keeps 16-byte LDS reads conflict-free).
+// rows are copied as 52 aligned dwords into a 208-byte LDS row (208/16 odd
+// keeps 16-byte LDS reads conflict-free) plus word 52 of each row apart.
 constexpr int kSlotBytesQ4K = kTileRows * 144;
 constexpr int kSlotBytesQ5K = kTileRows * 176;
-constexpr int kSlotBytesQ6K = kTileRows * 240;
+constexpr int kSlotBytesQ6K = kTileRows * 208 + 4 * kTileRows;
 
 struct KqDesc {
     const uint8_t* w;
@@ -42,10 +45,6 @@ struct KqDesc {
     float* y;
     int64_t ldx, ldy;
     int64_t row_bytes;
-    int64_t cost_base;  // weight bytes of the launch before this tensor (segment units)
-    int64_t cost_end;   // cost_base + this tensor's segments * seg_cost
-    int64_t seg_cost;   // bytes of one full segment: 64 * S * block_bytes
-    double inv_seg_cost;  // 1 / seg_cost, for a division-free segment search
     int32_t rows;
     int32_t nb;         // super-blocks per row
     int32_t fmt;
@@ -54,29 +53,31 @@ struct KqDesc {
     int32_t seg;        // S: super-blocks per segment (the last one of a row may be shorter)
     int32_t part_base;  // first partial-sum slot (one per segment) in the workspace
     int32_t tile_base;  // first counter in the workspace
+    int32_t wg_base;    // first workgroup of this tensor
+    int32_t wg_count;   // P_i: workgroups of this tensor
+    int32_t seg_q;      // workgroup u of the tensor streams segments [u*seg_q + min(u, seg_r), ...),
+    int32_t seg_r;      //   seg_q + (u < seg_r) of them
     float* partials;    // this tensor's partial sums in the workspace: [segments][ntok][64]
     uint32_t* counters; // this tensor's arrival counters: one per tile, zero between calls
+    int64_t reserved[2];
 };
 static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
 
 // Read by every workgroup before anything else (in one batch).
 struct KqHead {
-    int64_t cost_q;       // workgroup w starts at cost w * cost_q + min(w, cost_r):
-    int32_t cost_r;       //   total_cost = grid * cost_q + cost_r
     int32_t n;
-    int64_t reserved[2];
-    int64_t cost_end[kMaxSet];  // t[i].cost_end; INT64_MAX past the last tensor
+    int32_t reserved[7];
+    int32_t wg_end[kMaxSet];  // t[i].wg_base + t[i].wg_count; INT32_MAX past the last tensor
 };
-static_assert(sizeof(KqHead) == 160, "head is five 32-byte groups");
+static_assert(sizeof(KqHead) == 96, "head is three 32-byte groups");
 
 struct KqLaunch {
     KqHead h;
     KqDesc t[kMaxSet];
     float* partials;      // workspace base: [segments][ntok][64]
     uint32_t* counters;   // workspace base: one per tile
-    int64_t total_cost;   // sum of seg_cost * segments over the set
     int32_t ntok;
-    int32_t grid;         // persistent workgroups
+    int32_t grid;         // workgroups
     int32_t lds_bytes;
     int32_t total_segments;
 };
@@ -95,8 +96,13 @@ void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t
 // Checks (no HIP calls) of a set; KQ_OK or a KQ_ERR_* code.
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok);
 
-// Fills `out` (workspace pointers and grid left unset) and the workspace
-// sizes.  Assumes validate_set passed.
+// Fills `out` (workspace pointers and the workgroup split left unset) and
+// the workspace sizes.  Assumes validate_set passed.
 int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out, KqPlanSizes* sizes);
+
+// Splits the launch's workgroups between its tensors for at most
+// `capacity` workgroups: sets wg_base, wg_count, seg_q, seg_r of every
+// tensor, the head's wg_end and the grid.
+void assign_workgroups(KqLaunch* L, int32_t capacity);
 
 }  // namespace kq
