@@ -575,6 +575,19 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A wave whose column arrives late gets the SIMD first: on a launch that
+// lasts about as long as the memory system takes to deliver its bytes, the
+// waves served last would otherwise share their SIMD's VALU with waves that
+// are not on the critical path.  Ticks of the 100 MHz real-time counter
+// since the run started: 3, 4.5 and 6 us raise the priority to 1, 2, 3 (a
+// large matrix runs at 3 after its first columns, the same for every wave).
+__device__ __forceinline__ void late_priority(uint64_t t_start) {
+    const uint64_t dt = __builtin_amdgcn_s_memrealtime() - t_start;
+    if (dt > 600) __builtin_amdgcn_s_setprio(3);
+    else if (dt > 450) __builtin_amdgcn_s_setprio(2);
+    else if (dt > 300) __builtin_amdgcn_s_setprio(1);
+}
+
 // ------------------------------------------------------------ a run of segments
 // Segments j0..j1-1 of tensor T (tile-major), one super-block column at a
 // time.  DEPTH columns are in flight in DEPTH register sets used in turn:
@@ -606,6 +619,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
         __syncthreads();                                /* earlier reads of the slot done */   \
         float sx[NTOK];                                                                        \
         c[k_].commit(slot, sx);                                                                \
+        late_priority(t_start);                                                                \
         {                                                                                      \
             const bool valid = ij < j1;                                                        \
             c[k_].stage(T, offs, itile, ib, valid);                                            \
@@ -647,6 +661,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
 
 template <class Col, int NTOK, int DEPTH>
 __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int j0, int j1, uint8_t* slot) {
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
     static_assert(DEPTH >= 1 && DEPTH <= 3, "1..3 register sets");
     const int nseg = T.nseg, nb = T.nb, smask = T.seg - 1;
     int tile = j0 / nseg;
