@@ -12,8 +12,9 @@ synthetic data (kqgen) resident in HBM before the timed region.
 
 Prints ONE JSON line: effective weight GB/s over the whole step (launch gaps
 included), the roofline of the set kernel (bytes per launch / the average
-launch duration from HIP events recorded on the launch stream), and the CPU
-oracle's rate on a bounded sample on this host.
+launch duration from HIP events recorded on the launch stream), the CPU
+oracle's rate on a bounded sample on this host, and (default workload) the
+other configurations' figures with a streaming-read calibration.
 """
 from __future__ import annotations
 
@@ -64,6 +65,8 @@ def parse():
                    choices=["stream52", "qkvg_set", "lm_head", "single_q4k", "kv_pair"])
     p.add_argument("--ntok", type=int, default=1, help="kv_pair only")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-other-configs", action="store_true",
+                   help="skip the per-configuration figures and the read calibration")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES bytes (counter calibration) and exit")
@@ -91,10 +94,8 @@ def main():
         print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    import kqgen
     import quant_matvec_amd as kq
 
     if not os.path.exists(kq.LIB_PATH):
@@ -110,70 +111,22 @@ def main():
         return
 
     launches, wname, ntok = build_workload(args.workload, args.ntok)
-    print("[bench] generating %s (%d launches)" % (wname, len(launches)), file=sys.stderr, flush=True)
+    r = run_workload(launches, wname, ntok, args.steps, args.warmup, dev, keep_host=not args.no_cpu_baseline)
+    n_launch = r["launches"]
+    bytes_per_launch = r["algo_bytes"] / n_launch
+    achieved_gbs = bytes_per_launch / (r["us_per_launch_kernel"] * 1e-6) / 1e9
+    value = r["weight_bytes"] * args.steps / r["elapsed"] / 1e9
+    ms_per_step = r["elapsed"] / args.steps * 1e3
+    weight_bytes = r["weight_bytes"]
+    avg_launch_us = r["us_per_launch_kernel"]
 
-    # ---- inputs resident in HBM
-    sets = []
-    weight_bytes = 0
-    algo_bytes = 0
-    keep = []
-    host = []      # the same seeded inputs, kept for the CPU baseline
-    for launch in launches:
-        xs = {}
-        members = []
-        for T in launch:
-            w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
-            x = kqgen.activations(ntok, T.cols, *T.xkey)
-            host.append((T, w, x))
-            dw = torch.from_numpy(w.reshape(-1)).to(dev)
-            if T.xkey not in xs:
-                xs[T.xkey] = torch.from_numpy(x).to(dev)
-                algo_bytes += ntok * T.cols * 4
-            dy = torch.empty((ntok, T.rows), dtype=torch.float32, device=dev)
-            keep += [dw, dy]
-            members.append(dict(fmt=T.fmt, w=dw, x=xs[T.xkey], y=dy, rows=T.rows, cols=T.cols))
-            weight_bytes += T.weight_bytes
-            algo_bytes += T.weight_bytes + ntok * T.rows * 4
-        keep += list(xs.values())
-        sets.append(kq.make_set(members))
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-    n_launch = len(sets)
-
-    def step():
-        for s in sets:
-            kq.kq_matvec_set(s, ntok=ntok, stream=sptr)
-
-    # ---- warmup (also allocates the per-stream workspace outside the timed region)
-    for _ in range(max(1, args.warmup)):
-        step()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K steps, synchronized on both sides. HIP events on the
-    # launch stream bracket the same region; with the launches back to back,
-    # their span over all launches is the kernel's average launch duration
-    # (per-launch event pairs would add their own queue time to a ~20 us kernel).
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg_launch_us = ev0.elapsed_time(ev1) * 1e3 / (args.steps * n_launch)
-    bytes_per_launch = algo_bytes / n_launch
-    achieved_gbs = bytes_per_launch / (avg_launch_us * 1e-6) / 1e9
-
-    ms_per_step = elapsed / args.steps * 1e3
-    value = weight_bytes * args.steps / elapsed / 1e9
+    others = None
+    if args.workload == "stream52" and not args.no_other_configs:
+        others = other_configs(dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(host, ntok, args.cpu_seconds)
+        cpu = cpu_baseline(r["host"], ntok, args.cpu_seconds)
 
     out = {
         "metric": "effective weight GB/s (and % of HBM peak) + us per QKV+gate set, ntok=1",
@@ -197,7 +150,122 @@ def main():
                      "kernel": "kq_matvec_kernel<1>", "bytes_per_launch": int(bytes_per_launch)},
         "cpu_baseline": cpu,
     }
+    if others is not None:
+        out["other_configs"] = others
     print(json.dumps(out), flush=True)
+
+
+def run_workload(launches, wname, ntok, steps, warmup, dev, keep_host=False):
+    """Upload the seeded inputs of `launches` (one kq_matvec_set call each),
+    warm up, then time `steps` passes over them back to back.  Returns the
+    wall-clock time of the timed region and the launches' average duration
+    from two HIP events recorded on the launch stream around it."""
+    import torch
+
+    import kqgen
+    import quant_matvec_amd as kq
+
+    print("[bench] generating %s (%d launches)" % (wname, len(launches)), file=sys.stderr, flush=True)
+    sets = []
+    weight_bytes = 0
+    algo_bytes = 0
+    keep = []
+    host = []      # the same seeded inputs, kept for the CPU baseline
+    for launch in launches:
+        xs = {}
+        members = []
+        for T in launch:
+            w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+            x = kqgen.activations(ntok, T.cols, *T.xkey)
+            if keep_host:
+                host.append((T, w, x))
+            dw = torch.from_numpy(w.reshape(-1)).to(dev)
+            if T.xkey not in xs:
+                xs[T.xkey] = torch.from_numpy(x).to(dev)
+                algo_bytes += ntok * T.cols * 4
+            dy = torch.empty((ntok, T.rows), dtype=torch.float32, device=dev)
+            keep += [dw, dy]
+            members.append(dict(fmt=T.fmt, w=dw, x=xs[T.xkey], y=dy, rows=T.rows, cols=T.cols))
+            weight_bytes += T.weight_bytes
+            algo_bytes += T.weight_bytes + ntok * T.rows * 4
+        keep += list(xs.values())
+        sets.append(kq.make_set(members))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    n_launch = len(sets)
+
+    def step():
+        for s in sets:
+            kq.kq_matvec_set(s, ntok=ntok, stream=sptr)
+
+    # ---- warmup (also allocates the per-stream workspace outside the timed region)
+    for _ in range(max(1, warmup)):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, synchronized on both sides. HIP events on the
+    # launch stream bracket the same region; with the launches back to back,
+    # their span over all launches is the kernel's average launch duration
+    # (per-launch event pairs would add their own queue time to a ~20 us kernel).
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    return {"launches": n_launch, "weight_bytes": weight_bytes, "algo_bytes": algo_bytes, "elapsed": elapsed,
+            "us_per_launch_kernel": ev0.elapsed_time(ev1) * 1e3 / (steps * n_launch), "host": host}
+
+
+def other_configs(dev):
+    """The remaining configurations, each timed like the main one (warm GPU,
+    launches back to back, HIP events around the timed region), and a plain
+    streaming read as the calibration of what HBM delivers to a trivial
+    kernel.  C2 rotates over 16 seeded copies of the layer so that its
+    weights come from HBM; C1 and C5 are small enough to stay in the caches
+    (reported hot)."""
+    import torch
+    from kqgen import workloads as wl
+
+    res = {}
+
+    def one(key, launches, name, ntok, steps, warmup):
+        r = run_workload(launches, name, ntok, steps, warmup, dev)
+        us = r["us_per_launch_kernel"]
+        res[key] = {"workload": name, "us_per_launch": round(us, 3),
+                    "weight_GBs": round(r["weight_bytes"] / r["launches"] / (us * 1e-6) / 1e9, 1)}
+
+    one("C1_single_q4k_hot", wl.single_q4k(), "single_q4k_256x6656", 1, 2000, 500)
+    one("C2_qkvg_set_x16_rotating", [wl.qkvg_layer(2, i) for i in range(16)], "qkvg_set_x16_rotating", 1, 100, 50)
+    one("C4_lm_head_q6k", wl.lm_head(), "lm_head_q6k_202048x6656", 1, 200, 100)
+    for ntok in (1, 2, 4, 8):
+        one("C5_kv_pair_ntok%d_hot" % ntok, wl.kv_pair() + wl.kv_pair(swapped=True),
+            "kv_pair_q6k_q5k_ntok%d" % ntok, ntok, 1000, 300)
+    torch.cuda.empty_cache()
+    # calibration: the library's trivial 16-byte streaming-read probe over 2 GiB
+    import quant_matvec_amd as kq
+    buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(20):
+        kq.kq_debug_read_probe(buf, sink)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        kq.kq_debug_read_probe(buf, sink)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = buf.numel() * 4 * 20 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    res["calibration_streaming_read"] = {"what": "kq_debug_read_probe: 16-byte nontemporal loads over 2 GiB, nothing else",
+                                         "GBs": round(gbs, 1), "hbm_peak_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(host, ntok, budget_s):

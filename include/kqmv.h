@@ -147,6 +147,17 @@ int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks,
 int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols,
                float* out, int64_t ldw, void* stream);
 
+/*
+ * Calibration export, not part of the matvec: one launch of a trivial
+ * streaming read over `bytes` bytes at buf (device, 16-byte aligned, bytes a
+ * positive multiple of 16), with 16-byte nontemporal loads and nothing else
+ * (eight in flight per thread, 32 workgroups of 256 a compute unit), so its rate
+ * is what HBM delivers to a kernel on this GPU.  sink: a device uint32 that
+ * is written only when a fixed XOR value turns up (callers ignore it).
+ * Returns KQ_OK or a negative KQ_ERR_* code (KQ_ERR_ROWS for a bad size).
+ */
+int kq_debug_read_probe(const void* buf, int64_t bytes, void* sink, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* kq_strerror(int code);
 

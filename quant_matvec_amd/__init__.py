@@ -23,7 +23,7 @@ STATUS = {
     -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE",
 }
 EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set",
-           "kq_unpack_blocks", "kq_dequant", "kq_strerror", "kq_version")
+           "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror", "kq_version")
 
 
 class KqError(RuntimeError):
@@ -63,6 +63,8 @@ def load() -> ctypes.CDLL:
         L.kq_unpack_blocks.restype = ctypes.c_int
         L.kq_dequant.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ctypes.c_int
+        L.kq_debug_read_probe.argtypes = [vp, i64, vp, vp]
+        L.kq_debug_read_probe.restype = ctypes.c_int
         L.kq_strerror.argtypes = [ctypes.c_int]
         L.kq_strerror.restype = ctypes.c_char_p
         L.kq_version.argtypes = []
@@ -112,6 +114,14 @@ def kq_strerror(code: int) -> str:
 
 def kq_version() -> int:
     return load().kq_version()
+
+
+def kq_debug_read_probe(buf, sink, stream=None) -> int:
+    """One trivial streaming-read launch over the whole of `buf` (a GPU
+    tensor, 16-byte multiple); `sink` a GPU int32 tensor (calibration)."""
+    nbytes = buf.numel() * buf.element_size()
+    return _check(load().kq_debug_read_probe(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+                  "kq_debug_read_probe")
 
 
 def _plane_stride(t, default: int) -> int:

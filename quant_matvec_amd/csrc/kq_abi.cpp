@@ -12,6 +12,7 @@
 namespace kq {
 
 int launch_matvec(const KqLaunch& L, hipStream_t stream);
+int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,
                   int32_t* mins, float* d, float* dmin, hipStream_t stream);
 int launch_dequant(int32_t fmt, const void* w, int64_t rows, int32_t nb, float* out, int64_t ldw,
@@ -33,14 +34,17 @@ static int32_t slot_bytes(int32_t fmt, int32_t ntok) {
 }
 
 // Segment length S: 2 super-blocks (18-27 KB per 64-row segment), except
-// for Q6_K matrices of at most kSmallRows rows, which take 1 (13 KB).  A
-// decode set then splits into runs of similar size (its small Q6_K K and V
-// would otherwise be the longest runs), while a large matrix keeps few
-// partial sums.  Depends on (fmt, rows, cols) only.
+// for matrices whose workgroups get few segments in any launch: Q6_K
+// matrices of at most kSmallRows rows and any matrix of at most kTinyRows
+// rows take 1.  A decode set then splits into runs of similar size (its
+// small Q6_K K and V would otherwise be the longest runs), a K/V-sized
+// launch into one-block runs, while a large matrix keeps few partial sums.
+// Depends on (fmt, rows, cols) only.
 constexpr int64_t kSmallRows = 16384;
+constexpr int64_t kTinyRows = 1024;
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg) {
     const int64_t nb = cols / 256;
-    const int32_t S = (fmt == KQ_Q6_K && rows <= kSmallRows) ? 1 : 2;
+    const int32_t S = ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
 }
@@ -311,6 +315,13 @@ int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols, float* ou
     if (ldw < cols) return KQ_ERR_STRIDE;
     if (rows * (cols / 256) > ((int64_t)1 << 31) * 255) return KQ_ERR_TOO_LARGE;
     return launch_dequant(fmt, w, rows, (int32_t)(cols / 256), out, ldw, static_cast<hipStream_t>(stream));
+}
+
+int kq_debug_read_probe(const void* buf, int64_t bytes, void* sink, void* stream) {
+    if (!buf || !sink) return KQ_ERR_NULL;
+    if (bytes <= 0 || (bytes & 15)) return KQ_ERR_ROWS;
+    if ((reinterpret_cast<uintptr_t>(buf) & 15) || (reinterpret_cast<uintptr_t>(sink) & 3)) return KQ_ERR_ALIGN;
+    return launch_read_probe(buf, bytes, static_cast<uint32_t*>(sink), static_cast<hipStream_t>(stream));
 }
 
 const char* kq_strerror(int code) {

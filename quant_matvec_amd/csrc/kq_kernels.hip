@@ -889,6 +889,38 @@ __global__ void kq_dequant_kernel(int32_t fmt, const uint8_t* w, int64_t rows, i
     (void)dmin;
 }
 
+// ------------------------------------------------------------ read probe
+// A trivial streaming read (16-byte nontemporal loads, eight in flight per
+// thread, XOR reduction): what HBM delivers to a kernel that does nothing
+// else, the calibration the matvec's bandwidth is read against.  Writes
+// *sink only if the XOR hits a fixed value, so the loads cannot be dropped.
+__global__ __launch_bounds__(256) void kq_read_probe_kernel(const u32x4* __restrict__ p, int64_t n,
+                                                             uint32_t* sink) {
+    constexpr int U = 8;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + (U - 1) * stride < n; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n; i += stride) acc ^= p[i].x;
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return KQ_ERR_HIP;
+    hipLaunchKernelGGL(kq_read_probe_kernel, dim3(cus * 32), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(buf), bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
 // ------------------------------------------------------------ launchers
 // At most two waves per SIMD: more resident waves (the kernel would fit
 // three at one token plane) spread the same bytes over more concurrent row

@@ -4,8 +4,9 @@
 //
 // Work decomposition.  Rows are taken 64 at a time (a TILE: one row per
 // lane of a wave64).  Each tile row is cut into SEGMENTS of S consecutive
-// super-blocks (S = 2, or 1 for a Q6_K matrix of at most 16384 rows); the
-// segments of a tensor are numbered tile-major.  The row results of a tile are the ordered sum
+// super-blocks (S = 2, or 1 for a Q6_K matrix of at most 16384 rows and for
+// any matrix of at most 1024 rows); the segments of a tensor are numbered
+// tile-major.  The row results of a tile are the ordered sum
 // ((0 + seg_0) + seg_1) + ... of its segment sums, each segment accumulated
 // block by block.  S depends only on the tensor's own shape, so a tensor
 // computes bitwise the same result alone or in a set, and whatever

@@ -109,6 +109,9 @@ def test_invalid_calls_fail_before_hip(lib):
     assert lib.kq_unpack_blocks(12, BASE + 4, 1, None, None, None, None, None, None) == -6
     assert lib.kq_dequant(14, BASE, 4, 512, BASE + (1 << 30), 256, None) == -7
     assert lib.kq_dequant(14, BASE, 4, 500, BASE + (1 << 30), 512, None) == -2
+    assert lib.kq_debug_read_probe(None, 256, BASE, None) == -5
+    assert lib.kq_debug_read_probe(BASE, 250, BASE + (1 << 30), None) == -3
+    assert lib.kq_debug_read_probe(BASE + 4, 256, BASE + (1 << 30), None) == -6
     with pytest.raises(kq.KqError):
         kq.kq_matvec(12, BASE, 256, 300, BASE + (1 << 30), BASE + (2 << 30), stream=0)
 
