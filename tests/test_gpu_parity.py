@@ -254,3 +254,14 @@ def test_stream_layers_sampled():
             idx = np.arange(0, T.rows, 7)
             y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey], row_idx=idx, nthreads=8)
             check_tol(ys[T.name][:, idx], y_ref, s, "layer " + T.name)
+
+
+def test_read_probe_runs():
+    """The streaming-read calibration launches and leaves its buffer alone."""
+    t = torch()
+    note("read probe over 64 MiB")
+    buf = t.arange(1 << 24, dtype=t.int32, device="cuda")
+    sink = t.zeros(1, dtype=t.int32, device="cuda")
+    kq.kq_debug_read_probe(buf, sink)
+    t.cuda.synchronize()
+    assert int(buf[12345]) == 12345 and int(buf[-1]) == (1 << 24) - 1
