@@ -27,10 +27,14 @@ int32_t block_bytes(int32_t fmt) {
     }
 }
 
-// LDS of one workgroup: the weight slot of one super-block column plus one
-// KB of x per token plane.
-static int32_t slot_bytes(int32_t fmt, int32_t ntok) {
-    return (fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K : kSlotBytesQ6K) + 1024 * ntok;
+// LDS of one workgroup: the weight slot of one step (a super-block column
+// of a 64-row tile, or the two columns of a segment of a 32-row tile) plus
+// one KB of x per token plane and column.
+int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
+    const bool pair = tile_rows == 32;
+    const int32_t w = fmt == KQ_Q4_K ? kSlotBytesQ4K : fmt == KQ_Q5_K ? kSlotBytesQ5K
+                    : pair ? kSlotBytesQ6KPair : kSlotBytesQ6K;
+    return w + 1024 * ntok * (pair ? 2 : 1);
 }
 
 // Segment length S: 2 super-blocks (18-27 KB per 64-row segment), except
@@ -40,13 +44,21 @@ static int32_t slot_bytes(int32_t fmt, int32_t ntok) {
 // small Q6_K K and V would otherwise be the longest runs), a K/V-sized
 // launch into one-block runs, while a large matrix keeps few partial sums.
 // Depends on (fmt, rows, cols) only.
+//
+// Tile rows: 32 for a matrix of more than kSmallRows rows and an even number
+// of blocks a row, else 64.  With 64-row tiles every wave of an XCD keeps the
+// L2 lines its 64 rows share between successive block columns live, more
+// than the L2 holds on a large matrix, and about a third of the lines are
+// read twice; 32-row tiles that take a segment (two columns) a step halve
+// that and stay near one read per line.
 constexpr int64_t kSmallRows = 16384;
 constexpr int64_t kTinyRows = 1024;
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg) {
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg, int32_t* tile_rows) {
     const int64_t nb = cols / 256;
     const int32_t S = ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
+    *tile_rows = (rows > kSmallRows && nb % 2 == 0) ? 32 : kTileRows;
 }
 
 static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
@@ -75,9 +87,9 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
         if (T.rows > INT32_MAX || rb * kTileRows >= ((int64_t)1 << 31) || T.ldx > ((int64_t)1 << 40) ||
             T.ldy > ((int64_t)1 << 40))
             return KQ_ERR_TOO_LARGE;
-        int32_t ns, sg;
-        plan_tensor(T.fmt, T.rows, T.cols, &ns, &sg);
-        items += ((T.rows + kTileRows - 1) / kTileRows) * ns;
+        int32_t ns, sg, tr;
+        plan_tensor(T.fmt, T.rows, T.cols, &ns, &sg, &tr);
+        items += ((T.rows + tr - 1) / tr) * ns;
         if (items > INT32_MAX / 2) return KQ_ERR_TOO_LARGE;
     }
     // outputs must not overlap each other or any input (hull of the strided ranges)
@@ -120,14 +132,14 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.row_bytes = (int64_t)D.nb * block_bytes(T.fmt);
         D.rows = (int32_t)T.rows;
         D.fmt = T.fmt;
-        D.tiles = (int32_t)((T.rows + kTileRows - 1) / kTileRows);
-        plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg);
+        plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg, &D.tile_rows);
+        D.tiles = (int32_t)((T.rows + D.tile_rows - 1) / D.tile_rows);
         D.part_base = parts;
         parts += D.tiles * D.nseg;
         D.tile_base = tiles;
         tiles += D.tiles;
         segs += D.tiles * D.nseg;
-        if (slot_bytes(T.fmt, ntok) > lds) lds = slot_bytes(T.fmt, ntok);
+        if (slot_bytes(T.fmt, ntok, D.tile_rows) > lds) lds = slot_bytes(T.fmt, ntok, D.tile_rows);
     }
     L->total_segments = segs;
     L->lds_bytes = lds;
@@ -143,7 +155,7 @@ static int64_t workgroups_for(const KqLaunch& L, int64_t C, int32_t* per_wg) {
     for (int i = 0; i < L.h.n; ++i) {
         const KqDesc& D = L.t[i];
         const int64_t segs = (int64_t)D.tiles * D.nseg;
-        const int64_t seg_bytes = (int64_t)kTileRows * (D.nb < D.seg ? D.nb : D.seg) * block_bytes(D.fmt);
+        const int64_t seg_bytes = (int64_t)D.tile_rows * (D.nb < D.seg ? D.nb : D.seg) * block_bytes(D.fmt);
         int64_t k = C / seg_bytes;
         if (k < 1) k = 1;
         if (k > segs) k = segs;
@@ -162,7 +174,7 @@ void assign_workgroups(KqLaunch* L, int32_t capacity) {
     int64_t lo = 0, hi = 0;
     for (int i = 0; i < n; ++i) {
         const KqDesc& D = L->t[i];
-        const int64_t bytes = (int64_t)D.tiles * kTileRows * D.row_bytes;
+        const int64_t bytes = (int64_t)D.rows * D.row_bytes;
         if (bytes > hi) hi = bytes;
     }
     while (lo < hi) {
@@ -175,12 +187,12 @@ void assign_workgroups(KqLaunch* L, int32_t capacity) {
     // workgroups left over go to the tensors in proportion to their bytes
     // (more resident waves keep more bytes in flight on a large launch)
     int64_t total = 0;
-    for (int i = 0; i < n; ++i) total += (int64_t)L->t[i].tiles * kTileRows * L->t[i].row_bytes;
+    for (int i = 0; i < n; ++i) total += (int64_t)L->t[i].rows * L->t[i].row_bytes;
     const int64_t slack = capacity - used;
     for (int i = 0; i < n; ++i) {
         const KqDesc& D = L->t[i];
         const int32_t segs = D.tiles * D.nseg;
-        const int64_t bytes = (int64_t)D.tiles * kTileRows * D.row_bytes;
+        const int64_t bytes = (int64_t)D.rows * D.row_bytes;
         int64_t p = (segs + k[i] - 1) / k[i] + (total > 0 ? (int64_t)((double)slack * (double)bytes / (double)total) : 0);
         P[i] = (int32_t)(p < segs ? p : segs);
     }

@@ -132,6 +132,24 @@ __device__ __forceinline__ float4 xread(const uint8_t* xslot, int t, int e) {
     return *reinterpret_cast<const float4*>(xslot + 1024 * t + 4 * e);
 }
 
+// The sum of x over a sub-block, as the lane's block needs it: from the one
+// column of a 64-row tile (Sx1), or from the lane's own column of the two a
+// 32-row tile computes at once (Sx2: even lanes the first, odd the second).
+// `idx` names the lane of the column's DPP reduction that holds the sum.
+template <int NTOK>
+struct Sx1 {
+    float v[NTOK];
+    __device__ __forceinline__ float get(int t, int idx) const { return lane_value(v[t], idx); }
+};
+template <int NTOK>
+struct Sx2 {
+    float v[2][NTOK];
+    __device__ __forceinline__ float get(int t, int idx) const {
+        const float a = lane_value(v[0][t], idx), b = lane_value(v[1][t], idx);
+        return (threadIdx.x & 1) ? b : a;
+    }
+};
+
 // End of one step of a block's multiply-adds: the step's accumulators are
 // complete here and no LDS read of a later step moves above this point.
 // With the x of the next step requested at the top of a step, this keeps two
@@ -157,9 +175,9 @@ struct K45 {
 };
 
 // One group g of a block: sub-blocks 2g (low nibbles) and 2g+1 (high).
-template <int FMT, int NTOK, int G>
+template <int FMT, int NTOK, int G, class SX>
 __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&qh)[8], const K4Scales& S,
-                                          const uint8_t* xslot, const float (&sx)[NTOK],
+                                          const uint8_t* xslot, const SX& sx,
                                           float (&ts_e)[NTOK], float (&ts_o)[NTOK], float (&tm)[NTOK]) {
     uint32_t qs[8];
     {
@@ -196,69 +214,16 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
     for (int t = 0; t < NTOK; ++t) {
         ts_e[t] = __builtin_fmaf(sc0, al[t], ts_e[t]);
         ts_o[t] = __builtin_fmaf(sc1, ah[t], ts_o[t]);
-        tm[t] = __builtin_fmaf(m0, lane_value(sx[t], 8 * (2 * G)), tm[t]);
-        tm[t] = __builtin_fmaf(m1, lane_value(sx[t], 8 * (2 * G + 1)), tm[t]);
+        tm[t] = __builtin_fmaf(m0, sx.get(t, 8 * (2 * G)), tm[t]);
+        tm[t] = __builtin_fmaf(m1, sx.get(t, 8 * (2 * G + 1)), tm[t]);
     }
 }
 
-// Per-lane staging offsets of a 64-row column: 16-byte chunk q = 64*i + lane
-// of the column is row q / C, chunk q % C, at byte offset row*row_bytes +
-// 16*chunk from the tile's first row; in LDS it lands at byte 16*q =
-// row*BB + 16*chunk.
-template <int C>
-struct K45Offsets {
-    uint32_t off[C];
-    __device__ __forceinline__ void init(const KqDesc& T) {
-        int lane = threadIdx.x;
-        // opaque to the optimizer, so these per-format offsets are formed
-        // here and not hoisted to the kernel entry for every format
-        asm volatile("" : "+v"(lane));
-#pragma unroll
-        for (int i = 0; i < C; ++i) {
-            const int q = 64 * i + lane;
-            const int r = q / C, c = q - (q / C) * C;
-            off[i] = (uint32_t)r * (uint32_t)T.row_bytes + 16u * c;
-        }
-    }
-};
-
-// Staging and compute of one super-block column of 64 rows.
-template <int FMT, int NTOK>
-struct K45Column {
-    static constexpr int C = K45<FMT>::C;
-    static constexpr int BB = K45<FMT>::BB;
-    typedef K45Offsets<C> Offsets;
-    uint4 stg[C];
-    XStage<NTOK> xs;
-
-    // Loads are branch-free: chunks of rows past the end of the tensor (in
-    // its last tile) are clamped to the last chunk of its last row, which
-    // every such chunk exceeds, so they read valid memory whose values are
-    // never used.
-    // `valid` false: the column lies past the run; every lane then reads the
-    // tensor's first 16 bytes (values unused), so that the loads and the
-    // registers they fill are the same on every path.
-    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
-        const int rows_here = min(kTileRows, T.rows - tile * kTileRows);
-        const uint32_t max_off = valid ? (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C - 1) : 0u;
-        gbytes_t col = gbytes(T.w) + (valid ? (size_t)tile * kTileRows * T.row_bytes + (size_t)b * BB : (size_t)0);
-#pragma unroll
-        for (int i = 0; i < C; ++i)
-            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
-        xs.load(T, valid ? b : 0);
-    }
-    __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
-        const int lane = threadIdx.x;
-#pragma unroll
-        for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
-        xs.template commit<32>(slot + K45<FMT>::WSLOT, sx);
-    }
-    // acc[t] += this column's contribution for the lane's row
-    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const float (&sx)[NTOK], float (&acc)[NTOK]) {
-        (void)T; (void)tile; (void)b;
-        const uint8_t* row = slot + threadIdx.x * BB;
-        const uint8_t* xslot = slot + K45<FMT>::WSLOT;
+// acc[t] += the contribution of the Q4_K/Q5_K block at `row` (LDS) with x
+// at xslot and x sums sx.
+template <int FMT, int NTOK, class SX>
+__device__ __forceinline__ void block_mac(const uint8_t* row, const uint8_t* xslot, const SX& sx, float (&acc)[NTOK]) {
+    {
         const uint4 hdr = lds_read4(row);
         uint32_t qh[8];
         if constexpr (FMT == KQ_Q5_K) {
@@ -286,6 +251,124 @@ struct K45Column {
             acc[t] = __builtin_fmaf(-dmin, tm[t], acc[t]);
         }
     }
+}
+
+// Per-lane staging offsets of a 64-row column: 16-byte chunk q = 64*i + lane
+// of the column is row q / C, chunk q % C, at byte offset row*row_bytes +
+// 16*chunk from the tile's first row; in LDS it lands at byte 16*q =
+// row*BB + 16*chunk.
+template <int C>
+struct K45Offsets {
+    uint32_t off[C];
+    __device__ __forceinline__ void init(const KqDesc& T) {
+        int lane = threadIdx.x;
+        // opaque to the optimizer, so these per-format offsets are formed
+        // here and not hoisted to the kernel entry for every format
+        asm volatile("" : "+v"(lane));
+#pragma unroll
+        for (int i = 0; i < C; ++i) {
+            const int q = 64 * i + lane;
+            const int r = q / C, c = q - (q / C) * C;
+            off[i] = (uint32_t)r * (uint32_t)T.row_bytes + 16u * c;
+        }
+    }
+};
+
+// Staging and compute of one super-block column of 64 rows.
+template <int FMT, int NTOK>
+struct K45Column {
+    static constexpr int TR = kTileRows, CPS = 1;               // tile rows, columns a step
+    typedef Sx1<NTOK> Sx;
+    static constexpr int C = K45<FMT>::C;
+    static constexpr int BB = K45<FMT>::BB;
+    typedef K45Offsets<C> Offsets;
+    uint4 stg[C];
+    XStage<NTOK> xs;
+
+    // Loads are branch-free: chunks of rows past the end of the tensor (in
+    // its last tile) are clamped to the last chunk of its last row, which
+    // every such chunk exceeds, so they read valid memory whose values are
+    // never used.
+    // `valid` false: the column lies past the run; every lane then reads the
+    // tensor's first 16 bytes (values unused), so that the loads and the
+    // registers they fill are the same on every path.
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
+        const int rows_here = min(kTileRows, T.rows - tile * kTileRows);
+        const uint32_t max_off = valid ? (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C - 1) : 0u;
+        gbytes_t col = gbytes(T.w) + (valid ? (size_t)tile * kTileRows * T.row_bytes + (size_t)b * BB : (size_t)0);
+#pragma unroll
+        for (int i = 0; i < C; ++i)
+            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
+        xs.load(T, valid ? b : 0);
+    }
+    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
+        xs.template commit<32>(slot + K45<FMT>::WSLOT, sx.v);
+    }
+    // acc[t] += this column's contribution for the lane's row
+    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
+                                                   const Sx& sx, float (&acc)[NTOK]) {
+        (void)T; (void)tile; (void)b;
+        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, sx, acc);
+    }
+};
+
+// A 32-row tile of a Q4_K/Q5_K matrix, one segment (blocks b, b+1) a step.
+// Chunk q = 64*i + lane of a step is row q / 2C, 16-byte chunk q % 2C of the
+// row's two blocks (contiguous in memory), and lands in LDS at byte 16*q,
+// so row r's two blocks sit at r*2*BB and r*2*BB + BB.  Lane 2r + k
+// computes block b + k of row r, with column b + k's x.
+template <int FMT, int NTOK>
+struct K45Pair {
+    static constexpr int TR = 32, CPS = 2;                     // tile rows, columns a step
+    typedef Sx2<NTOK> Sx;
+    static constexpr int C = K45<FMT>::C, BB = K45<FMT>::BB, C2 = 2 * C;
+    static constexpr int N = TR * C2 / 64;                     // loads a lane: C
+    static constexpr int WSLOT = TR * 2 * BB;
+    struct Offsets {
+        uint32_t off[N];
+        __device__ __forceinline__ void init(const KqDesc& T) {
+            int lane = threadIdx.x;
+            asm volatile("" : "+v"(lane));
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int q = 64 * i + lane;
+                const int r = q / C2, c = q - (q / C2) * C2;
+                off[i] = (uint32_t)r * (uint32_t)T.row_bytes + 16u * c;
+            }
+        }
+    };
+    uint4 stg[N];
+    XStage<NTOK> xs0, xs1;
+
+    // Branch-free, clamped like the 64-row column (rows past the tensor's
+    // end read its last row's last chunk; `valid` false reads the tensor's
+    // first bytes and x of columns 0 and 1, which every such tensor has).
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
+        const int rows_here = min(TR, T.rows - tile * TR);
+        const uint32_t max_off = valid ? (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C2 - 1) : 0u;
+        gbytes_t col = gbytes(T.w) + (valid ? (size_t)tile * TR * T.row_bytes + (size_t)b * BB : (size_t)0);
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
+        xs0.load(T, valid ? b : 0);
+        xs1.load(T, valid ? b + 1 : 1);
+    }
+    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
+        xs0.template commit<32>(slot + WSLOT, sx.v[0]);
+        xs1.template commit<32>(slot + WSLOT + 1024 * NTOK, sx.v[1]);
+    }
+    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
+                                                   const Sx& sx, float (&acc)[NTOK]) {
+        (void)T; (void)tile; (void)b;
+        const int lane = threadIdx.x, k = lane & 1;
+        block_mac<FMT, NTOK>(slot + (lane >> 1) * 2 * BB + k * BB, slot + WSLOT + k * 1024 * NTOK, sx, acc);
+    }
 };
 
 // -------------------------------------------------------------------- Q6_K
@@ -308,9 +391,9 @@ __device__ __forceinline__ void q6_read4(const uint8_t* row, int i, uint32_t sh,
     o[3] = __builtin_amdgcn_alignbit(e, a.w, sh);
 }
 
-template <int NTOK, int N, int KH>
+template <int NTOK, int N, int KH, class SX>
 __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, const uint32_t (&scw)[4],
-                                               const uint8_t* xslot, const float (&sx)[NTOK],
+                                               const uint8_t* xslot, const SX& sx,
                                                float (&tl)[NTOK], float (&th)[NTOK]) {
     uint32_t A[4], B[4], H[4];
     q6_read4(row, 16 * N + 4 * KH, sh, A);          // ql bytes 64N + 16KH ..
@@ -380,11 +463,38 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
         const float off = (c < 2) ? -0x1p-19f : -0x1p-15f;
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
-            const float u = __builtin_fmaf(off, lane_value(sx[t], 4 * j), a[c][t]);
+            const float u = __builtin_fmaf(off, sx.get(t, 4 * j), a[c][t]);
             if (c < 2) tl[t] = __builtin_fmaf(scj, u, tl[t]);
             else th[t] = __builtin_fmaf(scj, u, th[t]);
         }
     }
+}
+
+// acc[t] += the contribution of the Q6_K block whose aligned words start at
+// `row` (LDS), shifted by sh bits, with word 52 given apart; x at xslot, x
+// sums sx.
+template <int NTOK, class SX>
+__device__ __forceinline__ void q6_block_mac(const uint8_t* row, uint32_t w52, uint32_t sh, const uint8_t* xslot,
+                                             const SX& sx, float (&acc)[NTOK]) {
+    // words 48..51 (scales) and word 52 (scales 14-15 and d, or d alone)
+    const uint4 s4 = lds_read4(row + 4 * 48);
+    uint32_t scw[4];
+    scw[0] = __builtin_amdgcn_alignbit(s4.y, s4.x, sh);
+    scw[1] = __builtin_amdgcn_alignbit(s4.z, s4.y, sh);
+    scw[2] = __builtin_amdgcn_alignbit(s4.w, s4.z, sh);
+    scw[3] = __builtin_amdgcn_alignbit(w52, s4.w, sh);
+    const float d = f16_to_f32((w52 >> sh) & 0xFFFFu);
+    float tl[NTOK], th[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
+    q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, sx, tl, th);
+    q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, sx, tl, th);
+    q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, sx, tl, th);
+    q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, sx, tl, th);
+    const float d24 = d * kTwo24;
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t)
+        acc[t] = __builtin_fmaf(d24, __builtin_fmaf(th[t], 0.0625f, tl[t]), acc[t]);
 }
 
 // Per-lane staging offsets of a 64-row Q6_K column.  Chunk q = 64*i + lane
@@ -425,6 +535,8 @@ struct Q6Offsets {
 
 template <int NTOK, bool ALT>
 struct Q6Column {
+    static constexpr int TR = kTileRows, CPS = 1;               // tile rows, columns a step
+    typedef Sx1<NTOK> Sx;
     static constexpr int SUB = 16;
     static constexpr int WSLOT = kTileRows * kQ6LdsRow + 4 * kTileRows;
     typedef Q6Offsets<ALT> Offsets;
@@ -463,54 +575,103 @@ struct Q6Column {
         tailv = *(const __attribute__((address_space(1))) uint16_t*)(gbytes(T.w) + (tail ? last + 208 : 0));
         xs.load(T, valid ? b : 0);
     }
-    __device__ __forceinline__ void commit(uint8_t* slot, float (&sx)[NTOK]) const {
+    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
         const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < kQ6Chunks; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         reinterpret_cast<uint32_t*>(slot + kTileRows * kQ6LdsRow)[lane] = lane == tail_row ? tailv : w52;
-        xs.template commit<16>(slot + WSLOT, sx);
+        xs.template commit<16>(slot + WSLOT, sx.v);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const float (&sx)[NTOK], float (&acc)[NTOK]) {
+                                                   const Sx& sx, float (&acc)[NTOK]) {
         const int lane = threadIdx.x;
-        const uint8_t* row = slot + lane * kQ6LdsRow;
-        const uint8_t* xslot = slot + WSLOT;
         // the block starts 2 bytes into its first staged word when its index
         // in the tensor, (r0+lane)*nb + b, is odd
         const uint32_t sh = !ALT ? 16u * (uint32_t)(b & 1)
                                  : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
-        // words 48..51 (scales) and word 52 (scales 14-15 and d, or d alone)
-        const uint32_t w52 = lds_read1(slot + kTileRows * kQ6LdsRow + 4 * lane);
-        const uint4 s4 = lds_read4(row + 4 * 48);
-        uint32_t scw[4];
-        scw[0] = __builtin_amdgcn_alignbit(s4.y, s4.x, sh);
-        scw[1] = __builtin_amdgcn_alignbit(s4.z, s4.y, sh);
-        scw[2] = __builtin_amdgcn_alignbit(s4.w, s4.z, sh);
-        scw[3] = __builtin_amdgcn_alignbit(w52, s4.w, sh);
-        const float d = f16_to_f32((w52 >> sh) & 0xFFFFu);
-        float tl[NTOK], th[NTOK];
+        q6_block_mac<NTOK>(slot + lane * kQ6LdsRow, lds_read1(slot + kTileRows * kQ6LdsRow + 4 * lane), sh,
+                           slot + WSLOT, sx, acc);
+    }
+};
+
+// A 32-row tile of a Q6_K matrix with an even number of blocks a row, one
+// segment (blocks b, b+1, b even) a step.  A row's two blocks are 420 bytes
+// from a 4-byte-aligned start: words 0..103 go as 26 16-byte chunks
+// (chunk q = 64*i + lane of the step is row q / 26, chunk q % 26; it lands
+// at LDS byte 16*q), word 104 (lane = row) into a separate 32-word array.
+// Lane 2r + k computes block b + k of row r: block b from word 0, block b+1
+// from word 52 two bytes in; its word 52 is the pair's word 104.  The pair
+// ends where the row does, so nothing past the tensor is read.
+template <int NTOK>
+struct Q6Pair {
+    static constexpr int TR = 32, CPS = 2;                     // tile rows, columns a step
+    typedef Sx2<NTOK> Sx;
+    static constexpr int CH = 26;                              // chunks of a row's pair
+    static constexpr int ROWB = 16 * CH;                       // 416: odd multiple of 16
+    static constexpr int N = TR * CH / 64;                     // loads a lane: 13
+    static constexpr int WSLOT = TR * ROWB + 4 * TR;
+    struct Offsets {
+        uint32_t off[N];
+        uint32_t off104;
+        __device__ __forceinline__ void init(const KqDesc& T) {
+            int lane = threadIdx.x;
+            asm volatile("" : "+v"(lane));
+            const uint32_t rb = (uint32_t)T.row_bytes;
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
-        q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, sx, tl, th);
-        q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, sx, tl, th);
-        q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, sx, tl, th);
-        q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, sx, tl, th);
-        const float d24 = d * kTwo24;
+            for (int i = 0; i < N; ++i) {
+                const uint32_t q = 64u * i + (uint32_t)lane;
+                const uint32_t r = q / CH, c = q - r * CH;
+                off[i] = r * rb + 16u * c;
+            }
+            off104 = ((uint32_t)lane & 31u) * rb + 416u;
+        }
+    };
+    uint4 stg[N];
+    uint32_t w104;
+    XStage<NTOK> xs0, xs1;
+
+    __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
+        const int rows_here = min(TR, T.rows - tile * TR);
+        const uint32_t rb = (uint32_t)T.row_bytes;
+        const uint32_t max_off = valid ? (uint32_t)(rows_here - 1) * rb + 16u * (CH - 1) : 0u;
+        const uint32_t max104 = valid ? (uint32_t)(rows_here - 1) * rb + 416u : 0u;
+        gbytes_t col = gbytes(T.w) + (valid ? (size_t)tile * TR * T.row_bytes + (size_t)210 * b : (size_t)0);
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t)
-            acc[t] = __builtin_fmaf(d24, __builtin_fmaf(th[t], 0.0625f, tl[t]), acc[t]);
+        for (int i = 0; i < N; ++i)
+            stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
+        w104 = *(const __attribute__((address_space(1))) uint32_t*)(col + min(o.off104, max104));
+        xs0.load(T, valid ? b : 0);
+        xs1.load(T, valid ? b + 1 : 1);
+    }
+    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+        const int lane = threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
+        reinterpret_cast<uint32_t*>(slot + TR * ROWB)[lane & 31] = w104;     // lanes 32..63 repeat 0..31
+        xs0.template commit<16>(slot + WSLOT, sx.v[0]);
+        xs1.template commit<16>(slot + WSLOT + 1024 * NTOK, sx.v[1]);
+    }
+    static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
+                                                   const Sx& sx, float (&acc)[NTOK]) {
+        (void)T; (void)tile; (void)b;
+        const int lane = threadIdx.x, k = lane & 1, r = lane >> 1;
+        const uint8_t* rowp = slot + r * ROWB + k * 208;
+        const uint32_t w52 = k ? lds_read1(slot + TR * ROWB + 4 * r) : lds_read1(rowp + 208);
+        q6_block_mac<NTOK>(rowp, w52, k ? 16u : 0u, slot + WSLOT + k * 1024 * NTOK, sx, acc);
     }
 };
 
 // ------------------------------------------------------------ tile results
-// Write a tile's 64 row results.
-template <int NTOK>
+// Write a tile's row results: lane = row of a 64-row tile; of a 32-row tile
+// the even lane of the pair that holds the row.
+template <int NTOK, int TR>
 __device__ __forceinline__ void write_rows(const KqDesc& T, int tile, const float (&v)[NTOK]) {
     const int lane = threadIdx.x;
-    const int r0 = tile * kTileRows;
-    if (lane < T.rows - r0) {
+    const int r = TR == kTileRows ? lane : lane >> 1;
+    const int r0 = tile * TR;
+    if ((TR == kTileRows || (lane & 1) == 0) && r < T.rows - r0) {
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t) gfloat(T.y)[t * T.ldy + r0 + lane] = v[t];
+        for (int t = 0; t < NTOK; ++t) gfloat(T.y)[t * T.ldy + r0 + r] = v[t];
     }
 }
 
@@ -533,7 +694,7 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L
 // the last contributor reads the partials only after its increment
 // returned; it adds all segment sums of the tile in order and resets the
 // counter for the next launch.
-template <int NTOK>
+template <int NTOK, int TR>
 __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int tile, int count) {
     const int lane = threadIdx.x;
     __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + tile);
@@ -571,7 +732,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
             }
         }
     }
-    write_rows<NTOK>(T, tile, sum);
+    write_rows<NTOK, TR>(T, tile, sum);
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -608,16 +769,16 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
 // of the run.  S is 1 or 2, so b is a segment's last block when
 // (b & smask) == smask, smask = S - 1.  All of it is 32-bit scalar
 // arithmetic (segment counts fit in int32).
-#define KQ_LAST_OF_SEG(b_) (((b_) & smask) == smask)
+#define KQ_LAST_OF_SEG(b_) (Col::CPS == 2 || ((b_) & smask) == smask)
 #define KQ_ADVANCE(t_, b_, j_)                                      \
     {                                                               \
-        if ((b_) + 1 == nb) { ++(t_); (b_) = 0; ++(j_); }             \
-        else { (j_) += KQ_LAST_OF_SEG(b_) ? 1 : 0; ++(b_); }          \
+        if ((b_) + Col::CPS >= nb) { ++(t_); (b_) = 0; ++(j_); }      \
+        else { (j_) += KQ_LAST_OF_SEG(b_) ? 1 : 0; (b_) += Col::CPS; } \
     }
 #define KQ_STEP(k_)                                                                            \
     {                                                                                          \
         __syncthreads();                                /* earlier reads of the slot done */   \
-        float sx[NTOK];                                                                        \
+        typename Col::Sx sx;                                                                   \
         c[k_].commit(slot, sx);                                                                \
         late_priority(t_start);                                                                \
         {                                                                                      \
@@ -625,15 +786,18 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
             c[k_].stage(T, offs, itile, ib, valid);                                            \
             if (valid) KQ_ADVANCE(itile, ib, ij)                                               \
         }                                                                                      \
-        const bool row_end = b + 1 == nb;                                                      \
+        const bool row_end = b + Col::CPS >= nb;                                               \
         const bool seg_end = row_end || KQ_LAST_OF_SEG(b);                                     \
         const int ntile = row_end ? tile + 1 : tile;                                           \
-        const int nbb = row_end ? 0 : b + 1;                                                   \
+        const int nbb = row_end ? 0 : b + Col::CPS;                                            \
         const int nj = seg_end ? j + 1 : j;                                                    \
         const bool has_next = nj < j1;                                                         \
         __syncthreads();                                /* slot written */                     \
         Col::compute(T, slot, tile, b, sx, acc);                                               \
         if (seg_end) {                                                                         \
+            if constexpr (Col::TR != kTileRows) {       /* the pair's two blocks */            \
+                _Pragma("unroll") for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + dpp_xor1(acc[t]); \
+            }                                                                                  \
             if (owned) {                                                                       \
                 _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = tsum[t] + acc[t];   \
             } else {                                                                           \
@@ -643,10 +807,10 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
             _Pragma("unroll") for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;                    \
             if (row_end || !has_next) {                                                        \
                 if (owned) {                                                                   \
-                    write_rows<NTOK>(T, tile, tsum);                                           \
+                    write_rows<NTOK, Col::TR>(T, tile, tsum);                                  \
                     _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = 0.0f;           \
                 } else {                                                                       \
-                    arrive<NTOK>(T, L, tile, pending);                                         \
+                    arrive<NTOK, Col::TR>(T, L, tile, pending);                                \
                     pending = 0;                                                               \
                 }                                                                              \
             }                                                                                  \
@@ -731,6 +895,15 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     const int u = w - T.wg_base;
     const int j0 = u * T.seg_q + min(u, T.seg_r);
     const int j1 = j0 + T.seg_q + (u < T.seg_r ? 1 : 0);
+    constexpr int DP = NTOK == 1 ? 2 : 1;       // 32-row tiles: segments in flight
+    if (T.tile_rows != kTileRows) {
+        switch (T.fmt) {
+        case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+        case KQ_Q5_K: run_segments<K45Pair<KQ_Q5_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+        default: run_segments<Q6Pair<NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+        }
+        return;
+    }
     switch (T.fmt) {
     case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;
     case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, L, j0, j1, slot); break;

@@ -39,6 +39,10 @@ constexpr int kMaxSet = KQ_MAX_SET;
 constexpr int kSlotBytesQ4K = kTileRows * 144;
 constexpr int kSlotBytesQ5K = kTileRows * 176;
 constexpr int kSlotBytesQ6K = kTileRows * 208 + 4 * kTileRows;
+// 32-row tiles stage the two blocks of a segment per step: Q4_K/Q5_K the
+// same bytes as a 64-row column; Q6_K 32 rows of 26 chunks (words 0..103
+// of the pair's 105) and word 104 of each row apart.
+constexpr int kSlotBytesQ6KPair = 32 * 416 + 4 * 32;
 
 struct KqDesc {
     const uint8_t* w;
@@ -60,7 +64,9 @@ struct KqDesc {
     int32_t seg_r;      //   seg_q + (u < seg_r) of them
     float* partials;    // this tensor's partial sums in the workspace: [segments][ntok][64]
     uint32_t* counters; // this tensor's arrival counters: one per tile, zero between calls
-    int64_t reserved[2];
+    int32_t tile_rows;  // 64, or 32 for a large matrix (two lanes a row, a segment a step)
+    int32_t reserved0;
+    int64_t reserved1;
 };
 static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
 
@@ -90,9 +96,12 @@ struct KqPlanSizes {
 
 int32_t block_bytes(int32_t fmt);
 
-// Segment length S (super-blocks) of one tensor and the segments per tile
-// row.  Depends on (fmt, rows, cols) only.
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg);
+// Segment length S (super-blocks) of one tensor, the segments per tile row
+// and the rows of a tile (64, or 32).  Depends on (fmt, rows, cols) only.
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg, int32_t* tile_rows);
+
+// LDS bytes of one column step of a tensor (weights, then x per token).
+int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows);
 
 // Checks (no HIP calls) of a set; KQ_OK or a KQ_ERR_* code.
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok);

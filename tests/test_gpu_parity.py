@@ -265,3 +265,57 @@ def test_read_probe_runs():
     kq.kq_debug_read_probe(buf, sink)
     t.cuda.synchronize()
     assert int(buf[12345]) == 12345 and int(buf[-1]) == (1 << 24) - 1
+
+
+# Matrices of more than 16384 rows with an even number of blocks a row run
+# in 32-row tiles (two lanes a row, a segment a step); an odd number keeps
+# 64-row tiles.  Rows 16461 leave a ragged last tile of 13 rows.
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,cols", [(16461, 6656), (16448, 512), (16449, 768)])
+def test_large_matrix_tiles_sampled(fmt, rows, cols):
+    w = kqgen.weights(fmt, rows, cols, 621, fmt, rows, cols)
+    x = kqgen.activations(1, cols, 622, cols)
+    note("large matrix fmt=%d %dx%d" % (fmt, rows, cols))
+    y = gpu_matvec(fmt, w, rows, cols, x, ldy=rows + 3)
+    assert np.isfinite(y).all()
+    rng = np.random.default_rng(11)
+    idx = np.unique(np.concatenate([np.arange(0, 96), np.arange(rows - 45, rows),
+                                    np.arange(31, rows, 32), rng.integers(0, rows, 600)]))
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, row_idx=idx, nthreads=8)
+    check_tol(y[:, idx], y_ref, s, "large fmt %d %dx%d" % (fmt, rows, cols))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("ntok", [2, 3, 8])
+def test_large_matrix_ntok_columns_bitwise(fmt, ntok):
+    """In 32-row tiles too, each column of an ntok call is bitwise the
+    ntok=1 call on that column."""
+    rows, cols = 16416, 2560
+    w = kqgen.weights(fmt, rows, cols, 623, fmt, ntok)
+    x = kqgen.activations(ntok, cols, 624, ntok)
+    note("large matrix ntok fmt=%d ntok=%d" % (fmt, ntok))
+    y = gpu_matvec(fmt, w, rows, cols, x)
+    for t in range(ntok):
+        y1 = gpu_matvec(fmt, w, rows, cols, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+    idx = np.arange(0, rows, 61)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, row_idx=idx, nthreads=8)
+    check_tol(y[:, idx], y_ref, s, "large ntok fmt %d" % fmt)
+
+
+def test_mixed_tile_set_matches_singles():
+    """A set of a 32-row-tile matrix and 64-row-tile ones: every member
+    bitwise equal to its own kq_matvec call."""
+    t = torch()
+    specs = [(Q6_K, 16448, 2560), (Q4_K, 4096, 2560), (Q5_K, 300, 2560)]
+    ws = [kqgen.weights(f, r, c, 625, i) for i, (f, r, c) in enumerate(specs)]
+    x = kqgen.activations(1, 2560, 626)
+    note("mixed tile set")
+    dx = dev(x)
+    dws = [dev(w.reshape(-1)) for w in ws]
+    ys = [t.full((1, r), float("nan"), dtype=t.float32, device="cuda") for (_, r, _) in specs]
+    kq.kq_matvec_set([dict(fmt=f, w=dw, x=dx, y=y, rows=r, cols=c)
+                      for (f, r, c), dw, y in zip(specs, dws, ys)], ntok=1)
+    for (f, r, c), w, y in zip(specs, ws, ys):
+        single = gpu_matvec(f, w, r, c, x)
+        assert np.array_equal(single.view(np.uint32), host(y).view(np.uint32)), (f, r)
