@@ -228,7 +228,8 @@ def other_configs(dev):
     streaming read as the calibration of what HBM delivers to a trivial
     kernel.  C2 rotates over 16 seeded copies of the layer so that its
     weights come from HBM; C1 and C5 are small enough to stay in the caches
-    (reported hot)."""
+    (reported hot).  The F1 lines are the rest of a layer's matvecs and the
+    Q5_K LM head, with their release formats (Ch 6 Figure 6.6)."""
     import torch
     from kqgen import workloads as wl
 
@@ -246,6 +247,23 @@ def other_configs(dev):
     for ntok in (1, 2, 4, 8):
         one("C5_kv_pair_ntok%d_hot" % ntok, wl.kv_pair() + wl.kv_pair(swapped=True),
             "kv_pair_q6k_q5k_ntok%d" % ntok, ntok, 1000, 300)
+    torch.cuda.empty_cache()
+    # the rest of a layer's matvecs (enough rotating copies that the weights
+    # come from HBM, not the 256 MB last-level cache), the Q5_K LM head, and
+    # whole layers in decode order (four launches a layer)
+    one("F1_attn_output_q4k_x24_rotating", [wl.attn_output(layer=i)[0] for i in range(24)],
+        "attn_output_q4k_6656x4096_x24", 1, 100, 50)
+    one("F1_ffn_gate_up_set_x4_rotating", [wl.ffn_gate_up(layer=i)[0] for i in range(4)],
+        "ffn_gate_up_q4k_2x19968x6656_x4", 1, 100, 50)
+    one("F1_ffn_down_q4k_x4_rotating", [wl.ffn_down(layer=2 * i)[0] for i in range(4)],
+        "ffn_down_q4k_6656x19968_x4", 1, 100, 50)
+    one("F1_ffn_down_q6k_x4_rotating", [wl.ffn_down(layer=2 * i + 1)[0] for i in range(4)],
+        "ffn_down_q6k_6656x19968_x4", 1, 100, 50)
+    one("F1_lm_head_q5k", wl.lm_head_q5k(), "lm_head_q5k_202048x6656", 1, 200, 100)
+    torch.cuda.empty_cache()
+    layers = [launch for i in range(4) for launch in wl.full_layer(layer=i)]
+    one("F1_full_layer_x4_rotating", layers, "full_layer_qkvg_o_gateup_down_x4", 1, 50, 20)
+    res["F1_full_layer_x4_rotating"]["us_per_layer"] = round(res["F1_full_layer_x4_rotating"]["us_per_launch"] * 4, 3)
     torch.cuda.empty_cache()
     # calibration: the library's trivial 16-byte streaming-read probe over 2 GiB
     import quant_matvec_amd as kq

@@ -1,6 +1,9 @@
 """The five synthetic workloads (shapes from muser-book Ch 13 sections 13.1
 and 13.6: hidden 6,656; 32 heads x 128 = 4,096 and 2 KV heads x 128 = 256
-outputs; 52 layers; and the 202,048-row LM-head scale of Ch 6 Figure 6.6).
+outputs; 52 layers; and the 202,048-row LM-head scale of Ch 6 Figure 6.6),
+and the rest of a layer's matvecs with the formats Ch 6 Figure 6.6 lists
+for them (attention output, FFN gate/up/down, the Q5_K LM head, the draft
+projections).
 
 Each workload is a list of "launches"; a launch is a list of tensors that
 share one grid-split call.  A tensor is (name, fmt, rows, cols, seed key,
@@ -17,6 +20,9 @@ Q_ROWS = 4096          # 32 heads x 128
 KV_ROWS = 256          # 2 KV heads x 128
 LAYERS = 52
 LM_ROWS = 202048
+FFN_ROWS = 19968       # ffn_gate/up outputs = ffn_down inputs
+DRAFT_ROWS = 1024      # draft k/v outputs
+DRAFT_FC_COLS = 33280  # draft fc inputs
 
 
 @dataclass(frozen=True)
@@ -63,6 +69,54 @@ def kv_pair(cfg: int = 5, swapped: bool = False):
     s = 1 if swapped else 0
     return [[Tensor("k", fk, KV_ROWS, HIDDEN, (cfg, s, 1), (cfg, s, 101)),
              Tensor("v", fv, KV_ROWS, HIDDEN, (cfg, s, 2), (cfg, s, 102))]]
+
+
+# The rest of a layer (Ch 6 Figure 6.6; Ch 13 section 13.6 puts o_proj at
+# about 6 % and the FFN at about 82 % of a layer's projection bytes).  In a
+# decode step each of these reads a different vector, so each is its own
+# launch; gate and up read the same normed hidden and share one.
+def attn_output(cfg: int = 6, layer: int = 0):
+    # 4096 -> 6656, Q4_K
+    return [[Tensor("attn_output", Q4_K, HIDDEN, Q_ROWS, (cfg, layer, 10), (cfg, layer, 110))]]
+
+
+def ffn_gate_up(cfg: int = 6, layer: int = 0):
+    # 6656 -> 19968 twice, Q4_K, one shared x
+    x = (cfg, layer, 111)
+    return [[Tensor("ffn_gate", Q4_K, FFN_ROWS, HIDDEN, (cfg, layer, 11), x),
+             Tensor("ffn_up", Q4_K, FFN_ROWS, HIDDEN, (cfg, layer, 12), x)]]
+
+
+def ffn_down(cfg: int = 6, layer: int = 0, fmt: int | None = None):
+    # 19968 -> 6656; the release artifact alternates Q4_K / Q6_K by layer
+    if fmt is None:
+        fmt = Q6_K if layer % 2 else Q4_K
+    return [[Tensor("ffn_down", fmt, HIDDEN, FFN_ROWS, (cfg, layer, 13), (cfg, layer, 113))]]
+
+
+def layer_rest(cfg: int = 6, layer: int = 0):
+    return attn_output(cfg, layer) + ffn_gate_up(cfg, layer) + ffn_down(cfg, layer)
+
+
+def full_layer(cfg: int = 6, layer: int = 0):
+    """A whole layer's projection matvecs in decode order: the Q/K/V/gate
+    set, the attention output, the FFN gate/up pair and the FFN down."""
+    qg = Q5_K if layer % 2 else Q4_K
+    return [qkvg_layer(cfg, layer, qg)] + layer_rest(cfg, layer)
+
+
+def lm_head_q5k(cfg: int = 7, rows: int = LM_ROWS):
+    # the LM head as the release artifact ships it: Q5_K, 6656 -> 202,048
+    return [[Tensor("lm_head_q5k", Q5_K, rows, HIDDEN, (cfg, 0, 0), (cfg, 0, 100))]]
+
+
+def draft_projections(cfg: int = 8):
+    """The draft model's k (Q4_K) and v (Q6_K), 6656 -> 1024 from one x, and
+    its fc, 33280 -> 6656 Q4_K."""
+    x = (cfg, 0, 100)
+    return [[Tensor("draft_k", Q4_K, DRAFT_ROWS, HIDDEN, (cfg, 0, 0), x),
+             Tensor("draft_v", Q6_K, DRAFT_ROWS, HIDDEN, (cfg, 0, 1), x)],
+            [Tensor("draft_fc", Q4_K, HIDDEN, DRAFT_FC_COLS, (cfg, 0, 2), (cfg, 0, 101))]]
 
 
 def total_weight_bytes(launches) -> int:

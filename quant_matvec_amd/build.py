@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     "-fno-fast-math", "-ffp-contract=off",
     # the packed-fp32 ALU forms stay off on this hardware
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # an atomic issued by one lane stays one atomic (no wave-level combining
+    # code around the fix-up counter)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -53,12 +53,20 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
 // that and stay near one read per line.
 constexpr int64_t kSmallRows = 16384;
 constexpr int64_t kTinyRows = 1024;
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg, int32_t* tile_rows) {
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
+                 int32_t* tile_rows) {
     const int64_t nb = cols / 256;
-    const int32_t S = ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
+    // A matrix of more than kTinyRows rows and an even number of blocks a row
+    // may run in 32-row tiles: always in two-block segments, whatever the
+    // token count, so that every token plane sums the same segments in the
+    // same order in either tile height.
+    const bool pairable = rows > kTinyRows && nb % 2 == 0;
+    const int32_t S = pairable ? 2 : ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
-    *tile_rows = (rows > kSmallRows && nb % 2 == 0) ? 32 : kTileRows;
+    // 32-row tiles at one token plane, and at two up to kSmallRows rows; with
+    // more planes the compute per byte grows and 64-row tiles run faster.
+    *tile_rows = pairable && (ntok == 1 || (ntok == 2 && rows <= kSmallRows)) ? 32 : kTileRows;
 }
 
 static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {
@@ -88,7 +96,7 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
             T.ldy > ((int64_t)1 << 40))
             return KQ_ERR_TOO_LARGE;
         int32_t ns, sg, tr;
-        plan_tensor(T.fmt, T.rows, T.cols, &ns, &sg, &tr);
+        plan_tensor(T.fmt, T.rows, T.cols, ntok, &ns, &sg, &tr);
         items += ((T.rows + tr - 1) / tr) * ns;
         if (items > INT32_MAX / 2) return KQ_ERR_TOO_LARGE;
     }
@@ -132,7 +140,7 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.row_bytes = (int64_t)D.nb * block_bytes(T.fmt);
         D.rows = (int32_t)T.rows;
         D.fmt = T.fmt;
-        plan_tensor(T.fmt, T.rows, T.cols, &D.nseg, &D.seg, &D.tile_rows);
+        plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.nseg, &D.seg, &D.tile_rows);
         D.tiles = (int32_t)((T.rows + D.tile_rows - 1) / D.tile_rows);
         D.part_base = parts;
         parts += D.tiles * D.nseg;

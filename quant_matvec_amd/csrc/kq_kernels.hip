@@ -307,11 +307,18 @@ struct K45Column {
         for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         xs.template commit<32>(slot + K45<FMT>::WSLOT, sx.v);
     }
-    // acc[t] += this column's contribution for the lane's row
+    // acc[t] += this column's contribution for the lane's row, formed on its
+    // own first (as a 32-row tile forms each block's), so that a segment
+    // sums to the same bits in either tile height
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
                                                    const Sx& sx, float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
-        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, sx, acc);
+        float c[NTOK];
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
+        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, sx, c);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
     }
 };
 
@@ -589,8 +596,13 @@ struct Q6Column {
         // in the tensor, (r0+lane)*nb + b, is odd
         const uint32_t sh = !ALT ? 16u * (uint32_t)(b & 1)
                                  : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
+        float c[NTOK];                  // formed on its own, as in K45Column
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
         q6_block_mac<NTOK>(slot + lane * kQ6LdsRow, lds_read1(slot + kTileRows * kQ6LdsRow + 4 * lane), sh,
-                           slot + WSLOT, sx, acc);
+                           slot + WSLOT, sx, c);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
     }
 };
 
@@ -895,14 +907,17 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     const int u = w - T.wg_base;
     const int j0 = u * T.seg_q + min(u, T.seg_r);
     const int j1 = j0 + T.seg_q + (u < T.seg_r ? 1 : 0);
-    constexpr int DP = NTOK == 1 ? 2 : 1;       // 32-row tiles: segments in flight
-    if (T.tile_rows != kTileRows) {
-        switch (T.fmt) {
-        case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
-        case KQ_Q5_K: run_segments<K45Pair<KQ_Q5_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
-        default: run_segments<Q6Pair<NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+    // 32-row tiles are planned for one and two token planes only
+    if constexpr (NTOK <= 2) {
+        constexpr int DP = NTOK == 1 ? 2 : 1;   // 32-row tiles: segments in flight
+        if (T.tile_rows != kTileRows) {
+            switch (T.fmt) {
+            case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+            case KQ_Q5_K: run_segments<K45Pair<KQ_Q5_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+            default: run_segments<Q6Pair<NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+            }
+            return;
         }
-        return;
     }
     switch (T.fmt) {
     case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;

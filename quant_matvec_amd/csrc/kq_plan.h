@@ -98,7 +98,8 @@ int32_t block_bytes(int32_t fmt);
 
 // Segment length S (super-blocks) of one tensor, the segments per tile row
 // and the rows of a tile (64, or 32).  Depends on (fmt, rows, cols) only.
-void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t* nseg, int32_t* seg, int32_t* tile_rows);
+void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
+                 int32_t* tile_rows);
 
 // LDS bytes of one column step of a tensor (weights, then x per token).
 int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows);

@@ -121,3 +121,20 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(kq, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         kq.kq_version()
+
+
+def test_release_shapes_match_the_pages():
+    """The rest-of-layer workloads against the figures the pages print:
+    the Q5_K LM head's bytes (Ch 6 section 6.5: 26 blocks x 176 B x 202,048
+    rows = 924,571,648 B) and the parameter counts of o_proj (27.3 M) and of
+    each FFN matrix (132.9 M) in Ch 13 section 13.6."""
+    from kqgen import workloads as wl
+    assert wl.total_weight_bytes(wl.lm_head_q5k()) == 924_571_648
+    [[o]] = wl.attn_output()
+    assert round(o.rows * o.cols / 1e6, 1) == 27.3
+    [[g, u]] = wl.ffn_gate_up()
+    [[d]] = wl.ffn_down()
+    for T in (g, u, d):
+        assert round(T.rows * T.cols / 1e6, 1) == 132.9
+    assert g.xkey == u.xkey and (g.rows, g.cols) == (d.cols, d.rows)
+    assert [T.fmt for layer in (0, 1) for [T] in wl.ffn_down(layer=layer)] == [12, 14]

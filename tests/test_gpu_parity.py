@@ -267,9 +267,10 @@ def test_read_probe_runs():
     assert int(buf[12345]) == 12345 and int(buf[-1]) == (1 << 24) - 1
 
 
-# Matrices of more than 16384 rows with an even number of blocks a row run
-# in 32-row tiles (two lanes a row, a segment a step); an odd number keeps
-# 64-row tiles.  Rows 16461 leave a ragged last tile of 13 rows.
+# Matrices of more than 1024 rows with an even number of blocks a row run
+# in 32-row tiles (two lanes a row, a segment a step) at one token plane,
+# and at two up to 16384 rows; otherwise, and with an odd number of blocks,
+# in 64-row tiles.  Rows 16461 leave a ragged last tile of 13 rows.
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("rows,cols", [(16461, 6656), (16448, 512), (16449, 768)])
 def test_large_matrix_tiles_sampled(fmt, rows, cols):
@@ -303,6 +304,24 @@ def test_large_matrix_ntok_columns_bitwise(fmt, ntok):
     check_tol(y[:, idx], y_ref, s, "large ntok fmt %d" % fmt)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("ntok", [2, 3, 8])
+def test_mid_matrix_ntok_columns_bitwise(fmt, ntok):
+    """A 4100-row matrix runs in 32-row tiles at one token plane and at two,
+    in 64-row tiles at three and eight: every column is still bitwise the
+    one-plane call on it (the same two-block segments, summed alike)."""
+    rows, cols = 4100, 2560
+    w = kqgen.weights(fmt, rows, cols, 625, fmt, ntok)
+    x = kqgen.activations(ntok, cols, 626, ntok)
+    note("mid matrix ntok fmt=%d ntok=%d" % (fmt, ntok))
+    y = gpu_matvec(fmt, w, rows, cols, x)
+    for t in range(ntok):
+        y1 = gpu_matvec(fmt, w, rows, cols, x[t:t + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
+    check_tol(y, y_ref, s, "mid ntok fmt %d" % fmt)
+
+
 def test_mixed_tile_set_matches_singles():
     """A set of a 32-row-tile matrix and 64-row-tile ones: every member
     bitwise equal to its own kq_matvec call."""
@@ -319,3 +338,49 @@ def test_mixed_tile_set_matches_singles():
     for (f, r, c), w, y in zip(specs, ws, ys):
         single = gpu_matvec(f, w, r, c, x)
         assert np.array_equal(single.view(np.uint32), host(y).view(np.uint32)), (f, r)
+
+
+# ---- the rest of a layer's matvecs and the other release shapes (Ch 6
+# Figure 6.6), at full size, each launch as the library runs it: attention
+# output (16 blocks a row), the FFN gate/up pair as one set, the FFN down
+# (78 blocks a row; Q4_K on even layers, Q6_K on odd), the Q5_K LM head and
+# the draft projections (130 blocks a row for the fc).
+
+def _sample_rows(rows, seed, tile=64):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([np.arange(0, rows, tile), np.arange(tile - 1, rows, tile),
+                                     np.arange(max(0, rows - 70), rows), rng.integers(0, rows, 1500)]))
+
+
+def _check_launch(launch, seed):
+    ws, xs = _set_inputs(launch, 1)
+    ys = _run_set(launch, ws, xs, 1)
+    for T in launch:
+        y = ys[T.name]
+        assert np.isfinite(y).all(), T.name
+        idx = _sample_rows(T.rows, seed)
+        y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey], row_idx=idx, nthreads=8)
+        check_tol(y[:, idx], y_ref, s, "%s %dx%d" % (T.name, T.rows, T.cols))
+        if len(launch) > 1:
+            single = gpu_matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey])
+            assert np.array_equal(single.view(np.uint32), y.view(np.uint32)), T.name
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_layer_rest_sampled(layer):
+    for k, launch in enumerate(wl.layer_rest(layer=layer)):
+        note("layer rest %d: %s" % (layer, ", ".join("%s fmt=%d %dx%d" % (T.name, T.fmt, T.rows, T.cols)
+                                                     for T in launch)))
+        _check_launch(launch, 40 + 3 * layer + k)
+
+
+def test_lm_head_q5k_sampled():
+    [launch] = wl.lm_head_q5k()
+    note("lm_head Q5_K 202048x6656 (full size)")
+    _check_launch(launch, 47)
+
+
+def test_draft_projections():
+    for k, launch in enumerate(wl.draft_projections()):
+        note("draft: " + ", ".join("%s fmt=%d %dx%d" % (T.name, T.fmt, T.rows, T.cols) for T in launch))
+        _check_launch(launch, 50 + k)
