@@ -10,7 +10,8 @@ marshalling only.  ``oracle.exact`` is an independent exact-rational
 re-statement used to pin the C oracle on tiny inputs.
 
 What is computed: muser-book Ch 13 section 13.1, y_i = sum_j W[i,j] x[j],
-with W decoded per muser-book Ch 6 sections 6.2-6.4.
+with W decoded per muser-book Ch 6 sections 6.2-6.4; and the embedding
+lookup of Ch 6 section 6.7, out[t] = row ids[t] of the dequantized table.
 """
 from __future__ import annotations
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
                                     ctypes.c_int64, ctypes.c_int32, i64p, ctypes.c_int64,
                                     f64p, f64p, ctypes.c_int32]
         L.oracle_matvec.restype = ctypes.c_int
+        L.oracle_embed.argtypes = [ctypes.c_int, u8p, ctypes.c_int64, ctypes.c_int64, i32p, ctypes.c_int64, f64p]
+        L.oracle_embed.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -111,6 +114,23 @@ def dequant(fmt: int, w: np.ndarray, rows: int, cols: int) -> np.ndarray:
     rc = lib().oracle_dequant(fmt, _ptr(w, ctypes.c_uint8), rows, cols, _ptr(out, ctypes.c_double))
     if rc:
         raise ValueError("bad format or cols")
+    return out
+
+
+def embed(fmt: int, w: np.ndarray, rows: int, cols: int, ids) -> np.ndarray:
+    """Embedding rows, float64 [n, cols]: row ids[t] of the dequantized
+    table, element by element (muser-book Ch 6 section 6.7); NaN rows for
+    ids outside [0, rows)."""
+    w = np.ascontiguousarray(w, dtype=np.uint8)
+    ids = np.ascontiguousarray(np.atleast_1d(ids), dtype=np.int32)
+    need = rows * (cols // 256) * block_bytes(fmt)
+    if w.size < need:
+        raise ValueError("weight buffer too small")
+    out = np.empty((ids.size, cols), np.float64)
+    rc = lib().oracle_embed(fmt, _ptr(w, ctypes.c_uint8), rows, cols, _ptr(ids, ctypes.c_int32), ids.size,
+                            _ptr(out, ctypes.c_double))
+    if rc:
+        raise ValueError("bad format, rows or cols")
     return out
 
 

@@ -173,6 +173,36 @@ int oracle_dequant(int fmt, const uint8_t* W, int64_t rows, int64_t cols, double
 }
 
 /*
+ * Embedding rows (Ch 6 section 6.7, the one-thread-per-output-element
+ * embedding lookup): out[t][j] = W[ids[t], j], the exact weight, for t < n
+ * and j < cols.  Each element is taken on its own, as that kernel does: the
+ * row starts at ids[t] * row_bytes with row_bytes = (cols/256) * block
+ * bytes (3,744 for a 6,656-wide Q4_K table, Ch 6 section 6.6); element j
+ * lies in block j/256 of the row, which is decoded and its element j % 256
+ * read out.  An id outside [0, rows) gives a row of NaN.  out is [n][cols]
+ * binary64.
+ */
+int oracle_embed(int fmt, const uint8_t* W, int64_t rows, int64_t cols, const int32_t* ids, int64_t n,
+                 double* out) {
+    int bb = oracle_block_bytes(fmt);
+    if (bb < 0 || cols <= 0 || cols % 256 || rows <= 0 || n < 0) return -1;
+    int64_t row_bytes = (cols / 256) * bb;
+    double w[256];
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t id = ids[t];
+        for (int64_t j = 0; j < cols; ++j) {
+            if (id < 0 || id >= rows) {
+                out[t * cols + j] = NAN;
+                continue;
+            }
+            if (oracle_dequant_block(fmt, W + id * row_bytes + (j / 256) * bb, w)) return -1;
+            out[t * cols + j] = w[j % 256];
+        }
+    }
+    return 0;
+}
+
+/*
  * y[t][k] = sum_j W[r_k, j] * x[t][j] and s[t][k] = sum_j |W[r_k, j] * x[t][j]|
  * for the rows r_k = row_idx[k] (k < n_out; row_idx NULL means r_k = k) and
  * tokens t < ntok.  x is [ntok][ldx] float32; y and s are [ntok][n_out]

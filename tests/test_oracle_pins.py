@@ -316,3 +316,54 @@ def test_row_selection_and_threads(oracle_lib, fmt):
     # s bounds |y|, and the rows really differ
     assert np.all(np.abs(y) <= s)
     assert len(set(y[0].tolist())) > 30
+
+
+def test_embedding_rows_handpacked(oracle_lib):
+    """The embedding lookup (Ch 6 section 6.7) on a table of hand-packed
+    Q4_K rows: a 6,656-wide row is 26 blocks, 3,744 bytes (Ch 6 section
+    6.6), and the row looked up for each id is d*sc_j*q - dmin*m_j of that
+    row's own blocks, exactly.  Ids repeat, come in any order, and ids
+    outside [0, rows) give rows of NaN."""
+    from oracle.exact import f16
+    rng = np.random.default_rng(77)
+    rows, cols, nb = 5, 6656, 26
+    table = bytearray()
+    fields = {}
+    for r in range(rows):
+        for b in range(nb):
+            d_bits, dmin_bits = _rand_f16_bits(rng, 2)
+            sc = [int(v) for v in rng.integers(0, 64, 8)]
+            m = [int(v) for v in rng.integers(0, 64, 8)]
+            q = [int(v) for v in rng.integers(0, 16, 256)]
+            table += kqpack.pack_q4k(d_bits, dmin_bits, sc, m, q)
+            fields[r, b] = (f16(d_bits & 255, d_bits >> 8), f16(dmin_bits & 255, dmin_bits >> 8), sc, m, q)
+    assert len(table) == rows * 3744
+    ids = [4, 0, 2, 2, -1, 5, 1, 1 << 30]
+    out = oracle_lib.embed(Q4_K, np.frombuffer(bytes(table), np.uint8), rows, cols, ids)
+    assert out.shape == (len(ids), cols)
+    for t, r in enumerate(ids):
+        if not 0 <= r < rows:
+            assert np.isnan(out[t]).all()
+            continue
+        for b in range(nb):
+            d, dmin, sc, m, q = fields[r, b]
+            for e in range(256):
+                assert Fraction(out[t, 256 * b + e]) == d * sc[e // 32] * q[e] - dmin * m[e // 32], (t, b, e)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_embedding_is_the_dequantized_row(oracle_lib, fmt):
+    """Element-by-element lookup against the block-by-block dequantization
+    of the whole table (another code path of the oracle), at widths of 1 and
+    26 blocks; a swapped pair of rows swaps the looked-up rows."""
+    for rows, cols in ((9, 256), (7, 6656)):
+        w = kqgen.weights(fmt, rows, cols, 88, fmt, cols)
+        ids = [rows - 1, 0, 3, 3, rows, -5]
+        out = oracle_lib.embed(fmt, w, rows, cols, ids)
+        full = oracle_lib.dequant(fmt, w, rows, cols)
+        assert np.array_equal(out[:4], full[ids[:4]])
+        assert np.isnan(out[4:]).all()
+        sw = w.copy()
+        sw[[0, 3]] = sw[[3, 0]]
+        out2 = oracle_lib.embed(fmt, sw, rows, cols, [0, 3, 1])
+        assert np.array_equal(out2, full[[3, 0, 1]])
