@@ -265,6 +265,8 @@ def other_configs(dev):
     one("F1_full_layer_x4_rotating", layers, "full_layer_qkvg_o_gateup_down_x4", 1, 50, 20)
     res["F1_full_layer_x4_rotating"]["us_per_layer"] = round(res["F1_full_layer_x4_rotating"]["us_per_launch"] * 4, 3)
     torch.cuda.empty_cache()
+    res.update(embedding_configs(dev))
+    torch.cuda.empty_cache()
     # calibration: the library's trivial 16-byte streaming-read probe over 2 GiB
     import quant_matvec_amd as kq
     buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -284,6 +286,46 @@ def other_configs(dev):
     del buf
     torch.cuda.empty_cache()
     return res
+
+
+def embedding_configs(dev):
+    """The embedding lookup (Ch 6 section 6.7) on the 202,048 x 6656 Q4_K
+    table: one id a call (a decode step) and 512 ids a call, each call with
+    fresh seeded ids.  Bytes moved = the rows read plus the float32 rows
+    written."""
+    import numpy as np
+    import torch
+
+    import kqgen
+    import quant_matvec_amd as kq
+    from kqgen import workloads as wl
+
+    T = wl.embedding_table()
+    print("[bench] generating the embedding table", file=sys.stderr, flush=True)
+    table = torch.from_numpy(kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey).reshape(-1)).to(dev)
+    row_bytes = T.weight_bytes // T.rows
+    out_res = {}
+    stream = torch.cuda.current_stream()
+    for n, calls in ((1, 2000), (512, 200)):
+        gen = np.random.default_rng(900 + n)
+        ids = torch.from_numpy(gen.integers(0, T.rows, size=n * calls, dtype=np.int32)).to(dev)
+        out = torch.empty((n, T.cols), dtype=torch.float32, device=dev)
+        for k in range(min(calls, 100)):
+            kq.kq_embed_rows(T.fmt, table, T.rows, T.cols, ids[k * n:(k + 1) * n], out, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for k in range(calls):
+            kq.kq_embed_rows(T.fmt, table, T.rows, T.cols, ids[k * n:(k + 1) * n], out, stream=stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / calls
+        moved = n * (row_bytes + T.cols * 4)
+        out_res["F3_embedding_q4k_%d_ids" % n] = {"workload": "embedding_q4k_202048x6656_%d_ids" % n,
+                                                 "us_per_call": round(us, 3),
+                                                 "GBs_moved": round(moved / (us * 1e-6) / 1e9, 1)}
+    del table
+    return out_res
 
 
 def cpu_baseline(host, ntok, budget_s):

@@ -68,6 +68,7 @@ enum kq_status {
 
 #define KQ_MAX_SET 16
 #define KQ_MAX_NTOK 8
+#define KQ_MAX_EMBED_IDS (1 << 24)
 
 /* One member of a grid-split set. */
 typedef struct kq_tensor {
@@ -119,6 +120,30 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
  * kq_matvec_set would return.
  */
 int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok);
+
+/*
+ * The embedding lookup of muser-book Ch 6 section 6.7: row ids[t] of a Q4_K
+ * table, dequantized, for t < n.
+ *   out[t][j] = d*sc_s*q - dmin*m_s of element j of row ids[t]
+ * (Ch 6 sections 6.2-6.3; s = sub-block of 32).  Each value is the exact
+ * weight correctly rounded to float32 (the products are exact, the
+ * difference is rounded once), so a row is bit-equal to kq_dequant of it.
+ *   fmt    only KQ_Q4_K: the pages admit a Q4_K (or F16) embedding table and
+ *          refuse anything else (Ch 6 section 6.1); other formats return
+ *          KQ_ERR_FORMAT.
+ *   table  device, rows x cols/256 blocks row-major (cols/256*144 bytes a
+ *          row, Ch 6 section 6.6), 16-byte aligned, owned by the caller.
+ *   ids    device int32 [n], 4-byte aligned; n in 1..KQ_MAX_EMBED_IDS.  An id
+ *          outside [0, rows) gives a row of NaN; nothing outside the table
+ *          is read.
+ *   out    device float32 [n][ldo], 16-byte aligned, ldo >= cols and a
+ *          multiple of 4; must not overlap the table or ids.
+ * Enqueued on `stream`; allocates nothing.  All checks run on the host
+ * before any HIP call.  Returns KQ_OK or a negative KQ_ERR_* code
+ * (KQ_ERR_ROWS for rows or n out of range).
+ */
+int kq_embed_rows(int32_t fmt, const void* table, int64_t rows, int64_t cols,
+                  const int32_t* ids, int32_t n, float* out, int64_t ldo, void* stream);
 
 /*
  * Debug/test export: integer decode of `nblocks` consecutive super-blocks

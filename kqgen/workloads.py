@@ -119,5 +119,11 @@ def draft_projections(cfg: int = 8):
             [Tensor("draft_fc", Q4_K, HIDDEN, DRAFT_FC_COLS, (cfg, 0, 2), (cfg, 0, 101))]]
 
 
+def embedding_table(cfg: int = 9, rows: int = LM_ROWS):
+    """The token embedding table: 202,048 x 6656 Q4_K, the ~1.34 B
+    parameters of Ch 13 section 13.6, the Q4_K table of Ch 6 section 6.5."""
+    return Tensor("token_embd", Q4_K, rows, HIDDEN, (cfg, 0, 0), (cfg, 0, 100))
+
+
 def total_weight_bytes(launches) -> int:
     return sum(t.weight_bytes for launch in launches for t in launch)

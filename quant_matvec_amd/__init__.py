@@ -23,7 +23,8 @@ STATUS = {
     -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE",
 }
 EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set",
-           "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror", "kq_version")
+           "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
+           "kq_version")
 
 
 class KqError(RuntimeError):
@@ -63,6 +64,8 @@ def load() -> ctypes.CDLL:
         L.kq_unpack_blocks.restype = ctypes.c_int
         L.kq_dequant.argtypes = [i32, vp, i64, i64, vp, i64, vp]
         L.kq_dequant.restype = ctypes.c_int
+        L.kq_embed_rows.argtypes = [i32, vp, i64, i64, vp, i32, vp, i64, vp]
+        L.kq_embed_rows.restype = ctypes.c_int
         L.kq_debug_read_probe.argtypes = [vp, i64, vp, vp]
         L.kq_debug_read_probe.restype = ctypes.c_int
         L.kq_strerror.argtypes = [ctypes.c_int]
@@ -175,6 +178,16 @@ def kq_unpack_blocks(fmt: int, w, nblocks: int, codes=None, scales=None, mins=No
     rc = load().kq_unpack_blocks(fmt, _ptr(w), nblocks, _ptr(codes), _ptr(scales), _ptr(mins), _ptr(d),
                                  _ptr(dmin), _stream(stream))
     _check(rc, "kq_unpack_blocks")
+
+
+def kq_embed_rows(fmt: int, table, rows: int, cols: int, ids, out, ldo: int | None = None,
+                  stream=None) -> None:
+    """out[t] = row ids[t] of the dequantized Q4_K table (device int32 ids,
+    device float32 out [n][ldo])."""
+    n = int(ids.numel()) if hasattr(ids, "numel") else len(ids)
+    ldo = _plane_stride(out, cols) if ldo is None else ldo
+    rc = load().kq_embed_rows(fmt, _ptr(table), rows, cols, _ptr(ids), n, _ptr(out), ldo, _stream(stream))
+    _check(rc, "kq_embed_rows")
 
 
 def kq_dequant(fmt: int, w, rows: int, cols: int, out, ldw: int | None = None, stream=None) -> None:

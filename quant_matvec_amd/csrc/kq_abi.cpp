@@ -17,6 +17,8 @@ int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, i
                   int32_t* mins, float* d, float* dmin, hipStream_t stream);
 int launch_dequant(int32_t fmt, const void* w, int64_t rows, int32_t nb, float* out, int64_t ldw,
                    hipStream_t stream);
+int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t* ids, int32_t n, float* out,
+                 int64_t ldo, hipStream_t stream);
 
 int32_t block_bytes(int32_t fmt) {
     switch (fmt) {
@@ -335,6 +337,29 @@ int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols, float* ou
     if (ldw < cols) return KQ_ERR_STRIDE;
     if (rows * (cols / 256) > ((int64_t)1 << 31) * 255) return KQ_ERR_TOO_LARGE;
     return launch_dequant(fmt, w, rows, (int32_t)(cols / 256), out, ldw, static_cast<hipStream_t>(stream));
+}
+
+int kq_embed_rows(int32_t fmt, const void* table, int64_t rows, int64_t cols, const int32_t* ids, int32_t n,
+                  float* out, int64_t ldo, void* stream) {
+    if (fmt != KQ_Q4_K) return KQ_ERR_FORMAT;
+    if (cols <= 0 || cols % 256) return KQ_ERR_COLS;
+    if (rows <= 0 || n < 1 || n > KQ_MAX_EMBED_IDS) return KQ_ERR_ROWS;
+    if (!table || !ids || !out) return KQ_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(table) & 15) || (reinterpret_cast<uintptr_t>(ids) & 3) ||
+        (reinterpret_cast<uintptr_t>(out) & 15))
+        return KQ_ERR_ALIGN;
+    if (ldo < cols || (ldo & 3)) return KQ_ERR_STRIDE;
+    const int64_t groups = (cols / 256 + 3) / 4;
+    if (rows > INT32_MAX || n * groups > INT32_MAX || ldo > ((int64_t)1 << 40)) return KQ_ERR_TOO_LARGE;
+    const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+    const uintptr_t o1 = o0 + (uintptr_t)(((int64_t)(n - 1) * ldo + cols) * 4);
+    const uintptr_t t0 = reinterpret_cast<uintptr_t>(table);
+    const uintptr_t t1 = t0 + (uintptr_t)(rows * (cols / 256) * 144);
+    const uintptr_t i0 = reinterpret_cast<uintptr_t>(ids);
+    const uintptr_t i1 = i0 + (uintptr_t)n * 4;
+    if (ranges_overlap(o0, o1, t0, t1) || ranges_overlap(o0, o1, i0, i1)) return KQ_ERR_OVERLAP;
+    return launch_embed(static_cast<const uint8_t*>(table), rows, cols, ids, n, out, ldo,
+                        static_cast<hipStream_t>(stream));
 }
 
 int kq_debug_read_probe(const void* buf, int64_t bytes, void* sink, void* stream) {

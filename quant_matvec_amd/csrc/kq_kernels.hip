@@ -929,6 +929,52 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     }
 }
 
+// ------------------------------------------------------------ embedding rows
+// The embedding lookup (muser-book Ch 6 section 6.7): out[t][j] is element j
+// of row ids[t] of a Q4_K table, dequantized.  A wave takes one block of one
+// row; lane l forms elements 4l..4l+3, which share a sub-block and a qs word
+// (low nibbles for the first 8 lanes of each 16, high for the next 8), and
+// stores them as one 16-byte write, so a wave writes the block's 1 KB
+// contiguously.  Four waves a workgroup take four consecutive blocks.
+// d*sc and dmin*m are exact in float32, and so is (d*sc)*q; the difference
+// is rounded once, so every value is the exact weight correctly rounded.
+__global__ __launch_bounds__(256) void kq_embed_kernel(const uint8_t* table, int64_t rows, int32_t nb,
+                                                        int32_t groups, const int32_t* ids, float* out,
+                                                        int64_t ldo) {
+    const int t = blockIdx.x / groups;
+    const int b = (blockIdx.x - t * groups) * 4 + (int)(threadIdx.x >> 6);
+    if (b >= nb) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t id = ids[t];
+    float4 v;
+    if (id < 0 || id >= rows) {
+        v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    } else {
+        const uint8_t* blk = table + (id * nb + b) * 144;
+        const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+        const int g = lane >> 4, hi = (lane >> 3) & 1, j = 2 * g + hi;
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(blk + 16 + 4 * (8 * g + (lane & 7)));
+        const uint32_t q = (word >> (4 * hi)) & 0x0F0F0F0Fu;
+        const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
+        const float dsc = f16_to_f32(hdr.x & 0xFFFFu) * (float)k4_sc(S, j);     // exact
+        const float dm = f16_to_f32(hdr.x >> 16) * (float)k4_m(S, j);           // exact
+        v.x = dsc * (float)(q & 0xFF) - dm;
+        v.y = dsc * (float)((q >> 8) & 0xFF) - dm;
+        v.z = dsc * (float)((q >> 16) & 0xFF) - dm;
+        v.w = dsc * (float)(q >> 24) - dm;
+    }
+    reinterpret_cast<float4*>(out + (int64_t)t * ldo + 256 * b)[lane] = v;
+}
+
+int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t* ids, int32_t n, float* out,
+                 int64_t ldo, hipStream_t stream) {
+    const int32_t nb = (int32_t)(cols / 256);
+    const int32_t groups = (nb + 3) / 4;
+    hipLaunchKernelGGL(kq_embed_kernel, dim3((unsigned)(n * groups)), dim3(256), 0, stream, table, rows, nb, groups,
+                       ids, out, ldo);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
 // ------------------------------------------------------------ debug kernels
 // One thread per super-block: fetch the block's aligned words, decode with
 // the same helpers as the matvec, expand to integers / float weights.

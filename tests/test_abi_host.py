@@ -138,3 +138,27 @@ def test_release_shapes_match_the_pages():
         assert round(T.rows * T.cols / 1e6, 1) == 132.9
     assert g.xkey == u.xkey and (g.rows, g.cols) == (d.cols, d.rows)
     assert [T.fmt for layer in (0, 1) for [T] in wl.ffn_down(layer=layer)] == [12, 14]
+
+
+def test_embed_rows_admission(lib):
+    """kq_embed_rows admits a Q4_K table only (the embedding fence of Ch 6
+    section 6.1) and checks sizes, alignment, strides and overlap on the
+    host; every call here fails before any HIP call."""
+    T, I, O = BASE, BASE + (1 << 30), BASE + (2 << 30)
+    good = dict(fmt=12, table=T, rows=202048, cols=6656, ids=I, n=4, out=O, ldo=6656)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return lib.kq_embed_rows(a["fmt"], a["table"], a["rows"], a["cols"], a["ids"], a["n"], a["out"],
+                                 a["ldo"], None)
+
+    for fmt in (13, 14, 0, 7):
+        assert call(fmt=fmt) == -1
+    assert call(cols=6600) == -2 and call(cols=0) == -2
+    assert call(rows=0) == -3 and call(n=0) == -3 and call(n=(1 << 24) + 1) == -3
+    assert call(table=None) == -5 and call(ids=None) == -5 and call(out=None) == -5
+    assert call(table=T + 8) == -6 and call(ids=I + 2) == -6 and call(out=O + 4) == -6
+    assert call(ldo=6652) == -7 and call(ldo=6658) == -7
+    # out over the table, or over the ids
+    assert call(out=T + 16) == -8
+    assert call(out=I - 64, n=1) == -8

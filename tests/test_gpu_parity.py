@@ -384,3 +384,57 @@ def test_draft_projections():
     for k, launch in enumerate(wl.draft_projections()):
         note("draft: " + ", ".join("%s fmt=%d %dx%d" % (T.name, T.fmt, T.rows, T.cols) for T in launch))
         _check_launch(launch, 50 + k)
+
+
+# ---- the embedding lookup (Ch 6 section 6.7): rows of a Q4_K table,
+# dequantized, bit for bit against the oracle's element-by-element lookup.
+
+def _gpu_embed(w, rows, cols, ids, ldo=None):
+    t = torch()
+    ldo = ldo or cols
+    table = dev(w.reshape(-1))
+    dids = dev(np.asarray(ids, np.int32))
+    out = t.full((len(ids), ldo), -7.0, dtype=t.float32, device="cuda")
+    kq.kq_embed_rows(Q4_K, table, rows, cols, dids, out, ldo=ldo)
+    o = host(out)
+    if ldo > cols:
+        assert (o[:, cols:] == -7.0).all(), "kernel wrote past cols"
+    return o[:, :cols]
+
+
+def _check_embed(o, ref, ids, rows):
+    for k, r in enumerate(ids):
+        if 0 <= r < rows:
+            assert np.array_equal(o[k].view(np.uint32), ref[k].astype(np.float32).view(np.uint32)), (k, r)
+        else:
+            assert np.isnan(o[k]).all() and np.isnan(ref[k]).all(), (k, r)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 768), (5, 256), (300, 6656)])
+def test_embed_rows_bit_exact(rows, cols):
+    w = kqgen.weights(Q4_K, rows, cols, 700, rows, cols)
+    ids = [0, rows - 1, 3 % rows, 3 % rows, -1, rows, 1 << 30] + list(range(1, rows, 7))
+    note("embed rows=%d cols=%d n=%d" % (rows, cols, len(ids)))
+    o = _gpu_embed(w, rows, cols, ids, ldo=cols + 4)
+    _check_embed(o, oracle.embed(Q4_K, w, rows, cols, ids), ids, rows)
+    # the same bits as the dequantization export on those rows
+    t = torch()
+    full = t.empty((rows, cols), dtype=t.float32, device="cuda")
+    kq.kq_dequant(Q4_K, dev(w.reshape(-1)), rows, cols, full)
+    fh = host(full)
+    for k, r in enumerate(ids):
+        if 0 <= r < rows:
+            assert np.array_equal(o[k].view(np.uint32), fh[r].view(np.uint32))
+
+
+def test_embed_rows_full_table_sampled():
+    """The 202,048 x 6656 Q4_K table at full size: a decode step's single
+    id, then a batch of ids with repeats and both ends of the table."""
+    T = wl.embedding_table()
+    w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+    note("embed full table 202048x6656")
+    rng = np.random.default_rng(5)
+    for ids in ([int(rng.integers(0, T.rows))],
+                [0, T.rows - 1, T.rows - 1] + [int(v) for v in rng.integers(0, T.rows, 40)]):
+        o = _gpu_embed(w, T.rows, T.cols, ids)
+        _check_embed(o, oracle.embed(T.fmt, w, T.rows, T.cols, ids), ids, T.rows)
