@@ -69,6 +69,7 @@ enum kq_status {
 #define KQ_MAX_SET 16
 #define KQ_MAX_NTOK 8
 #define KQ_MAX_EMBED_IDS (1 << 24)
+#define KQ_MAX_NTOK16 16
 
 /* One member of a grid-split set. */
 typedef struct kq_tensor {
@@ -120,6 +121,23 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
  * kq_matvec_set would return.
  */
 int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok);
+
+/*
+ * The same product as kq_matvec for ntok in 1..KQ_MAX_NTOK16 token planes
+ * (up to the 16-token verify width of muser-book Ch 6 section 6.8, whose
+ * weight-stationary tile this follows), computed on the matrix cores:
+ *   y[t][i] = sum_j W[i,j] x[t][j],  t < ntok.
+ * Arguments, layouts, alignment and errors as kq_matvec (w 16-byte aligned,
+ * x [ntok][ldx] 16-byte aligned with ldx >= cols a multiple of 4, y
+ * [ntok][ldy] 4-byte aligned with ldy >= rows, y disjoint from w and x),
+ * except KQ_ERR_NTOK for ntok outside 1..16.  Every weight byte is read
+ * once for all planes.  Results meet the same per-row tolerance as
+ * kq_matvec but are not bitwise equal to it (another reduction order); a
+ * plane's result does not depend on ntok.  Allocates nothing.
+ */
+int kq_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols,
+                const float* x, int64_t ldx, float* y, int64_t ldy,
+                int32_t ntok, void* stream);
 
 /*
  * The embedding lookup of muser-book Ch 6 section 6.7: row ids[t] of a Q4_K

@@ -19,6 +19,8 @@ int launch_dequant(int32_t fmt, const void* w, int64_t rows, int32_t nb, float* 
                    hipStream_t stream);
 int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t* ids, int32_t n, float* out,
                  int64_t ldo, hipStream_t stream);
+int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+                    int64_t ldy, int32_t ntok, hipStream_t stream);
 
 int32_t block_bytes(int32_t fmt) {
     switch (fmt) {
@@ -75,10 +77,10 @@ static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b
     return a0 < b1 && b0 < a1;
 }
 
-int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
+static int validate_tensors(const kq_tensor* t, int32_t n, int32_t ntok, int32_t max_ntok) {
     if (n < 1 || n > kMaxSet) return KQ_ERR_SET_SIZE;
     if (t == nullptr) return KQ_ERR_NULL;
-    if (ntok < 1 || ntok > KQ_MAX_NTOK) return KQ_ERR_NTOK;
+    if (ntok < 1 || ntok > max_ntok) return KQ_ERR_NTOK;
     int64_t items = 0;
     for (int i = 0; i < n; ++i) {
         const kq_tensor& T = t[i];
@@ -123,6 +125,8 @@ int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) {
     }
     return KQ_OK;
 }
+
+int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) { return validate_tensors(t, n, ntok, KQ_MAX_NTOK); }
 
 int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPlanSizes* sz) {
     *L = KqLaunch{};
@@ -317,6 +321,24 @@ int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols, const floa
     return kq_matvec_set(&t, 1, ntok, stream);
 }
 
+int kq_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+                int64_t ldy, int32_t ntok, void* stream) {
+    kq_tensor t;
+    t.fmt = fmt;
+    t.reserved = 0;
+    t.w = w;
+    t.x = x;
+    t.y = y;
+    t.rows = rows;
+    t.cols = cols;
+    t.ldx = ldx;
+    t.ldy = ldy;
+    const int rc = validate_tensors(&t, 1, ntok, KQ_MAX_NTOK16);
+    if (rc != KQ_OK) return rc;
+    if ((rows + 15) / 16 > INT32_MAX) return KQ_ERR_TOO_LARGE;
+    return launch_matvec16(fmt, w, rows, cols, x, ldx, y, ldy, ntok, static_cast<hipStream_t>(stream));
+}
+
 int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes_out, int32_t* scales_out,
                      int32_t* mins_out, float* d_out, float* dmin_out, void* stream) {
     if (block_bytes(fmt) < 0) return KQ_ERR_FORMAT;
@@ -375,7 +397,7 @@ const char* kq_strerror(int code) {
     case KQ_ERR_FORMAT: return "unsupported format (only Q4_K=12, Q5_K=13, Q6_K=14)";
     case KQ_ERR_COLS: return "cols must be a positive multiple of 256";
     case KQ_ERR_ROWS: return "rows (or block count) must be positive";
-    case KQ_ERR_NTOK: return "ntok must be in 1..8";
+    case KQ_ERR_NTOK: return "ntok must be in 1..8 (1..16 for kq_matvec16)";
     case KQ_ERR_NULL: return "null pointer";
     case KQ_ERR_ALIGN: return "misaligned pointer (w, x need 16 bytes; y 4 bytes)";
     case KQ_ERR_STRIDE: return "bad leading dimension (ldx >= cols and a multiple of 4; ldy >= rows)";

@@ -975,6 +975,179 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
+// ------------------------------------------------------------ up to 16 token planes on the matrix cores
+// A weight-stationary tile in the manner of the pages' 16-row verify kernel
+// (Ch 6 section 6.8): a one-wave workgroup owns 16 rows and walks all their
+// blocks once for every token plane.  Per block it issues 64 matrix-core
+// products v_mfma_f32_16x16x4_f32, C[row][token] += A[row][k] * B[k][token]:
+// - lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], so lane
+//   (r, g) = (l % 16, l / 16) brings row r's elements 64g..64g+63 of the block
+//   and token r's x over the same elements, one element a product;
+// - A is sc*q of the element (an integer below 2^13, exact in float32), B
+//   is x as given (float32), so the products are the pages' code times x;
+// - lane l ends with C[4(l/16) + i][l % 16], i < 4: four rows of one token.
+// Then C is scaled by the rows' d, and the min term dmin * sum_s m_s * sum(x
+// over sub-block s) is formed by two more products (A = m of the lane's two
+// sub-blocks, B = the token's x sums over them).  Everything is float32.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The 64 values sc*q of elements 64g..64g+63 of a block, in element order,
+// and (Q4_K/Q5_K) the mins of its two sub-blocks.
+template <int FMT>
+__device__ __forceinline__ void mm16_group(const uint8_t* blk, int g, float (&a)[64], float& m_lo, float& m_hi) {
+    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
+    const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
+    const float sl = (float)k4_sc(S, 2 * g), sh = (float)k4_sc(S, 2 * g + 1);
+    m_lo = (float)k4_m(S, 2 * g);
+    m_hi = (float)k4_m(S, 2 * g + 1);
+    constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;
+    const uint4 q0 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g);
+    const uint4 q1 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g + 16);
+    const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (FMT == KQ_Q5_K) {
+        const uint4 h0 = *reinterpret_cast<const uint4*>(blk + 16);
+        const uint4 h1 = *reinterpret_cast<const uint4*>(blk + 32);
+        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
+        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            uint32_t lo = (q[i] >> (8 * c)) & 15u, hi = (q[i] >> (8 * c + 4)) & 15u;
+            if constexpr (FMT == KQ_Q5_K) {
+                // fifth bit of element e: bit e/32 of qh[e % 32]
+                lo |= ((h[i] >> (8 * c + 2 * g)) & 1u) << 4;
+                hi |= ((h[i] >> (8 * c + 2 * g + 1)) & 1u) << 4;
+            }
+            a[4 * i + c] = sl * (float)lo;
+            a[32 + 4 * i + c] = sh * (float)hi;
+        }
+    }
+}
+
+// n consecutive 32-bit words from a 2-byte-aligned address inside a block:
+// aligned loads, realigned by 16 bits when the address is 2 mod 4.  The
+// extra aligned word read stays inside the block for every use below.
+template <int N>
+__device__ __forceinline__ void words_at(const uint8_t* p, uint32_t (&out)[N]) {
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
+    const uint32_t sh = (reinterpret_cast<uintptr_t>(p) & 2) ? 16u : 0u;
+    uint32_t w[N + 1];
+#pragma unroll
+    for (int i = 0; i <= N; ++i) w[i] = a[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
+}
+
+// Q6_K: elements 64g..64g+63 are n = g/2, k = 2(g%2) + j/32, l = j%32 of the
+// layout (ql[64n + 32(k%2) + l] nibble k/2, bits 2k..2k+1 of qh[32n + l]),
+// that is bytes j of ql[64n..], nibble g%2, and qh[32n + j%32]; sub-block
+// of 16 is 4g + j/16.
+__device__ __forceinline__ void mm16_group_q6(const uint8_t* blk, int g, float (&a)[64]) {
+    const int n = g >> 1, nib = 4 * (g & 1);
+    uint32_t ql[16], qh[8], scw[1];
+    words_at<16>(blk + 64 * n, ql);
+    words_at<8>(blk + 128 + 32 * n, qh);
+    words_at<1>(blk + 192 + 4 * g, scw);
+#pragma unroll
+    for (int j = 0; j < 64; ++j) {
+        const uint32_t lo4 = (ql[j >> 2] >> (8 * (j & 3) + nib)) & 15u;
+        const int k = 2 * (g & 1) + (j >> 5);
+        const uint32_t hb = (qh[(j & 31) >> 2] >> (8 * (j & 3) + 2 * k)) & 3u;
+        const int q = (int)(lo4 | (hb << 4)) - 32;
+        const float sc = (float)(int8_t)(scw[0] >> (8 * (j >> 4)));
+        a[j] = sc * (float)q;
+    }
+}
+
+template <int FMT>
+__global__ __launch_bounds__(64) void kq_matvec16_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows,
+                                                          int32_t nb, const float* x, int64_t ldx, int32_t ntok,
+                                                          float* y, int64_t ldy) {
+    constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
+    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    const int row0 = blockIdx.x * 16;
+    // A rows past the matrix repeat its last row; their results are not written
+    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
+    const bool tok_ok = r16 < ntok;
+    const float* xt = x + (int64_t)min(r16, ntok - 1) * ldx + 64 * g;
+    const uint8_t* orow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int b = 0; b < nb; ++b) {
+        float a[64];
+        float m_lo = 0.0f, m_hi = 0.0f;
+        if constexpr (FMT == KQ_Q6_K) mm16_group_q6(arow + (int64_t)b * BB, g, a);
+        else mm16_group<FMT>(arow + (int64_t)b * BB, g, a, m_lo, m_hi);
+        float xv[64];
+        const float4* xp = reinterpret_cast<const float4*>(xt + 256 * (int64_t)b);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float4 v = xp[i];
+            xv[4 * i] = tok_ok ? v.x : 0.0f;
+            xv[4 * i + 1] = tok_ok ? v.y : 0.0f;
+            xv[4 * i + 2] = tok_ok ? v.z : 0.0f;
+            xv[4 * i + 3] = tok_ok ? v.w : 0.0f;
+        }
+        f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
+        if constexpr (FMT == KQ_Q6_K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(orow[i] + (int64_t)b * BB + 208));
+                acc[i] = __builtin_fmaf(d, C[i], acc[i]);
+            }
+        } else {
+            float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) { slo += xv[j]; shi += xv[32 + j]; }
+            f32x4 C2 = {0.0f, 0.0f, 0.0f, 0.0f};
+            C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_lo, slo, C2, 0, 0, 0);
+            C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_hi, shi, C2, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t hw = *reinterpret_cast<const uint32_t*>(orow[i] + (int64_t)b * BB);
+                acc[i] = __builtin_fmaf(f16_to_f32(hw & 0xFFFFu), C[i], acc[i]);
+                acc[i] = __builtin_fmaf(-f16_to_f32(hw >> 16), C2[i], acc[i]);
+            }
+        }
+    }
+    if (tok_ok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = row0 + 4 * g + i;
+            if (r < rows) y[(int64_t)r16 * ldy + r] = acc[i];
+        }
+    }
+}
+
+int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+                    int64_t ldy, int32_t ntok, hipStream_t stream) {
+    const int32_t nb = (int32_t)(cols / 256);
+    const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
+    const dim3 grid((unsigned)((rows + 15) / 16));
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    switch (fmt) {
+    case KQ_Q4_K:
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q4_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
+        break;
+    case KQ_Q5_K:
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q5_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
+        break;
+    default:
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
+        break;
+    }
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
 // ------------------------------------------------------------ debug kernels
 // One thread per super-block: fetch the block's aligned words, decode with
 // the same helpers as the matvec, expand to integers / float weights.

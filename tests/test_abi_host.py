@@ -25,7 +25,7 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(kq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -162,3 +162,19 @@ def test_embed_rows_admission(lib):
     # out over the table, or over the ids
     assert call(out=T + 16) == -8
     assert call(out=I - 64, n=1) == -8
+
+
+def test_matvec16_admission(lib):
+    """kq_matvec16 takes 1..16 token planes and otherwise the checks of
+    kq_matvec, all on the host."""
+    W, X, Y = BASE, BASE + (1 << 30), BASE + (2 << 30)
+    assert lib.kq_matvec16(12, W, 256, 6656, X, 6656, Y, 256, 0, None) == -4
+    assert lib.kq_matvec16(12, W, 256, 6656, X, 6656, Y, 256, 17, None) == -4
+    assert lib.kq_matvec16(7, W, 256, 6656, X, 6656, Y, 256, 16, None) == -1
+    assert lib.kq_matvec16(12, W, 256, 6600, X, 6656, Y, 256, 16, None) == -2
+    assert lib.kq_matvec16(12, W, 0, 6656, X, 6656, Y, 256, 16, None) == -3
+    assert lib.kq_matvec16(12, None, 256, 6656, X, 6656, Y, 256, 16, None) == -5
+    assert lib.kq_matvec16(12, W + 4, 256, 6656, X, 6656, Y, 256, 16, None) == -6
+    assert lib.kq_matvec16(12, W, 256, 6656, X, 6654, Y, 256, 16, None) == -7
+    # y planes reaching into x
+    assert lib.kq_matvec16(12, W, 256, 6656, X, 6656, X - 4096, 256, 16, None) == -8

@@ -438,3 +438,60 @@ def test_embed_rows_full_table_sampled():
                 [0, T.rows - 1, T.rows - 1] + [int(v) for v in rng.integers(0, T.rows, 40)]):
         o = _gpu_embed(w, T.rows, T.cols, ids)
         _check_embed(o, oracle.embed(T.fmt, w, T.rows, T.cols, ids), ids, T.rows)
+
+
+# ---- up to 16 token planes on the matrix cores (kq_matvec16): the verify
+# width of Ch 6 section 6.8.
+
+def _gpu_matvec16(fmt, w_np, rows, cols, x_np, ldy=None):
+    t = torch()
+    x_np = np.atleast_2d(x_np).astype(np.float32)
+    ntok = x_np.shape[0]
+    ldy = ldy or rows
+    y = t.full((ntok, ldy), float("nan"), dtype=t.float32, device="cuda")
+    kq.kq_matvec16(fmt, dev(w_np.reshape(-1)), rows, cols, dev(x_np), y, ntok=ntok, ldy=ldy)
+    out = host(y)
+    if ldy > rows:
+        assert np.isnan(out[:, rows:]).all(), "kernel wrote past rows"
+    return out[:, :rows]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 16), (300, 6656, 16), (4100, 2560, 9), (16, 256, 1),
+                                            (1, 512, 16)])
+def test_matvec16_parity(fmt, rows, cols, ntok):
+    w = kqgen.weights(fmt, rows, cols, 800, fmt, rows, cols)
+    x = kqgen.activations(ntok, cols, 801, ntok, cols)
+    note("matvec16 fmt=%d %dx%d ntok=%d" % (fmt, rows, cols, ntok))
+    y = _gpu_matvec16(fmt, w, rows, cols, x, ldy=rows + 5)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=8)
+    check_tol(y, y_ref, s, "matvec16 fmt %d %dx%d ntok %d" % (fmt, rows, cols, ntok))
+    y2 = _gpu_matvec16(fmt, w, rows, cols, x, ldy=rows + 5)
+    assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_matvec16_plane_independent_of_ntok(fmt):
+    """A token plane's result is bitwise the same whatever ntok is."""
+    rows, cols = 200, 1536
+    w = kqgen.weights(fmt, rows, cols, 802, fmt)
+    x = kqgen.activations(16, cols, 803, fmt)
+    note("matvec16 planes fmt=%d" % fmt)
+    y16 = _gpu_matvec16(fmt, w, rows, cols, x)
+    for n in (1, 5, 11):
+        yn = _gpu_matvec16(fmt, w, rows, cols, x[:n])
+        assert np.array_equal(yn.view(np.uint32), y16[:n].view(np.uint32)), n
+
+
+def test_matvec16_release_shapes_sampled():
+    """Full-size release shapes at the 16-token verify width: the attention
+    output (Q4_K) and the Q6_K FFN down (78 blocks a row), rows sampled."""
+    for launch in (wl.attn_output(layer=0), wl.ffn_down(layer=1)):
+        [T] = launch[0]
+        w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+        x = kqgen.activations(16, T.cols, *T.xkey)
+        note("matvec16 %s fmt=%d %dx%d" % (T.name, T.fmt, T.rows, T.cols))
+        y = _gpu_matvec16(T.fmt, w, T.rows, T.cols, x)
+        idx = _sample_rows(T.rows, 60, tile=16)[:700]
+        y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, row_idx=idx, nthreads=8)
+        check_tol(y[:, idx], y_ref, s, "matvec16 " + T.name)
