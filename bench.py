@@ -267,6 +267,8 @@ def other_configs(dev):
     torch.cuda.empty_cache()
     res.update(embedding_configs(dev))
     torch.cuda.empty_cache()
+    res.update(matvec16_configs(dev))
+    torch.cuda.empty_cache()
     # calibration: the library's trivial 16-byte streaming-read probe over 2 GiB
     import quant_matvec_amd as kq
     buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -286,6 +288,62 @@ def other_configs(dev):
     del buf
     torch.cuda.empty_cache()
     return res
+
+
+def matvec16_configs(dev):
+    """16 token planes (the verify width) with kq_matvec16 on release shapes,
+    rotating copies so the weights come from HBM; each call reads the
+    weights once.  For context, the same weights through kq_matvec as two
+    8-plane calls."""
+    import torch
+
+    import kqgen
+    import quant_matvec_amd as kq
+    from kqgen import workloads as wl
+
+    out_res = {}
+    stream = torch.cuda.current_stream()
+    cases = [("attn_output_q4k_x24", [wl.attn_output(layer=i)[0][0] for i in range(24)], 200),
+             ("ffn_gate_q4k_x4", [wl.ffn_gate_up(layer=i)[0][0] for i in range(4)], 50),
+             ("lm_head_q5k", [wl.lm_head_q5k()[0][0]], 10)]
+    for name, tensors, reps in cases:
+        print("[bench] generating %s for 16 planes" % name, file=sys.stderr, flush=True)
+        mem = []
+        for T in tensors:
+            w = torch.from_numpy(kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey).reshape(-1)).to(dev)
+            x = torch.from_numpy(kqgen.activations(16, T.cols, *T.xkey)).to(dev)
+            y = torch.empty((16, T.rows), dtype=torch.float32, device=dev)
+            mem.append((T, w, x, y))
+        wbytes = sum(T.weight_bytes for T, _, _, _ in mem)
+        weights = sum(T.rows * T.cols for T, _, _, _ in mem)
+
+        def run16():
+            for T, w, x, y in mem:
+                kq.kq_matvec16(T.fmt, w, T.rows, T.cols, x, y, ntok=16, stream=stream.cuda_stream)
+
+        def run8x2():
+            for T, w, x, y in mem:
+                for h in (0, 8):
+                    kq.kq_matvec(T.fmt, w, T.rows, T.cols, x[h:h + 8], y[h:h + 8], ntok=8, stream=stream.cuda_stream)
+
+        for key, fn in (("kq_matvec16", run16), ("kq_matvec_2x8", run8x2)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / (reps * len(mem))
+            out_res["F2_%s_ntok16_%s" % (name, key)] = {
+                "workload": "%s_ntok16" % name, "entry": key, "us_per_tensor": round(us, 3),
+                "weight_GBs": round(wbytes / len(mem) / (us * 1e-6) / 1e9, 1),
+                "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2)}
+        del mem
+        torch.cuda.empty_cache()
+    return out_res
 
 
 def embedding_configs(dev):

@@ -991,74 +991,131 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
 // sub-blocks, B = the token's x sums over them).  Everything is float32.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// The 64 values sc*q of elements 64g..64g+63 of a block, in element order,
-// and (Q4_K/Q5_K) the mins of its two sub-blocks.
+// One block's operands for a lane: the raw bytes of its row's group g and
+// its token's x over the same 64 elements, and the headers of the block in
+// its four output rows.  Loads and use are split so that the next block's
+// loads are in flight while this block's products run.
 template <int FMT>
-__device__ __forceinline__ void mm16_group(const uint8_t* blk, int g, float (&a)[64], float& m_lo, float& m_hi) {
-    const uint4 hdr = *reinterpret_cast<const uint4*>(blk);
-    const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-    const float sl = (float)k4_sc(S, 2 * g), sh = (float)k4_sc(S, 2 * g + 1);
-    m_lo = (float)k4_m(S, 2 * g);
-    m_hi = (float)k4_m(S, 2 * g + 1);
-    constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;
-    const uint4 q0 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g);
-    const uint4 q1 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g + 16);
-    const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    uint32_t h[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if constexpr (FMT == KQ_Q5_K) {
-        const uint4 h0 = *reinterpret_cast<const uint4*>(blk + 16);
-        const uint4 h1 = *reinterpret_cast<const uint4*>(blk + 32);
-        h[0] = h0.x; h[1] = h0.y; h[2] = h0.z; h[3] = h0.w;
-        h[4] = h1.x; h[5] = h1.y; h[6] = h1.z; h[7] = h1.w;
-    }
+struct Mm16Raw {
+    uint4 hdr, q0, q1, h0, h1;        // Q4_K/Q5_K (h0, h1: Q5_K qh)
+    uint32_t ql[17], qh[9], scw[2];   // Q6_K aligned words
+    uint32_t sh;                      // Q6_K: realignment of the block (0 or 16)
+    uint32_t ohdr[4];                 // d|dmin (Q6_K: d) of the output rows
+    float4 xv[16];
+
+    __device__ __forceinline__ void load(const uint8_t* blk, const uint8_t* const (&oblk)[4], const float* xb,
+                                         int g) {
+        if constexpr (FMT == KQ_Q6_K) {
+            // n = g/2: ql[64n..64n+63], qh[32n..32n+31], scales 4g..4g+3, read as
+            // aligned words from the block's 4-byte-aligned base (the extra word
+            // of each run stays inside the block)
+            const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
+            sh = (reinterpret_cast<uintptr_t>(blk) & 2) ? 16u : 0u;
+            const int n = g >> 1;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 17; ++i) ql[i] = a[16 * n + i];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            uint32_t lo = (q[i] >> (8 * c)) & 15u, hi = (q[i] >> (8 * c + 4)) & 15u;
+            for (int i = 0; i < 9; ++i) qh[i] = a[32 + 8 * n + i];
+            scw[0] = a[48 + g];
+            scw[1] = a[49 + g];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint16_t*>(oblk[i] + 208);
+        } else {
+            constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;
+            hdr = *reinterpret_cast<const uint4*>(blk);
+            q0 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g);
+            q1 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g + 16);
             if constexpr (FMT == KQ_Q5_K) {
-                // fifth bit of element e: bit e/32 of qh[e % 32]
-                lo |= ((h[i] >> (8 * c + 2 * g)) & 1u) << 4;
-                hi |= ((h[i] >> (8 * c + 2 * g + 1)) & 1u) << 4;
+                h0 = *reinterpret_cast<const uint4*>(blk + 16);
+                h1 = *reinterpret_cast<const uint4*>(blk + 32);
             }
-            a[4 * i + c] = sl * (float)lo;
-            a[32 + 4 * i + c] = sh * (float)hi;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint32_t*>(oblk[i]);
+        }
+        const float4* xp = reinterpret_cast<const float4*>(xb);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] = xp[i];
+    }
+
+    // sc*q of elements 64g..64g+63 in element order, and (Q4_K/Q5_K) the
+    // mins of the two sub-blocks
+    __device__ __forceinline__ void codes(int g, float (&a)[64], float& m_lo, float& m_hi) const {
+        if constexpr (FMT == KQ_Q6_K) {
+            // element 64g + j is n = g/2, k = 2(g%2) + j/32, l = j%32 of the layout:
+            // byte j of the ql run (nibble g%2), bits 2k..2k+1 of qh[32n + j%32],
+            // sub-block of 16: 4g + j/16
+            const int nib = 4 * (g & 1);
+            m_lo = m_hi = 0.0f;
+            uint32_t L[16], H[8];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) L[i] = __builtin_amdgcn_alignbit(ql[i + 1], ql[i], sh);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) H[i] = __builtin_amdgcn_alignbit(qh[i + 1], qh[i], sh);
+            const uint32_t sc4 = __builtin_amdgcn_alignbit(scw[1], scw[0], sh);
+#pragma unroll
+            for (int j = 0; j < 64; ++j) {
+                const uint32_t lo4 = (L[j >> 2] >> (8 * (j & 3) + nib)) & 15u;
+                const int k = 2 * (g & 1) + (j >> 5);
+                const uint32_t hb = (H[(j & 31) >> 2] >> (8 * (j & 3) + 2 * k)) & 3u;
+                a[j] = (float)(int8_t)(sc4 >> (8 * (j >> 4))) * (float)((int)(lo4 | (hb << 4)) - 32);
+            }
+        } else {
+            const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
+            const float sl = (float)k4_sc(S, 2 * g), shs = (float)k4_sc(S, 2 * g + 1);
+            m_lo = (float)k4_m(S, 2 * g);
+            m_hi = (float)k4_m(S, 2 * g + 1);
+            const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+            const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t lo = (q[i] >> (8 * c)) & 15u, hi = (q[i] >> (8 * c + 4)) & 15u;
+                    if constexpr (FMT == KQ_Q5_K) {
+                        // fifth bit of element e: bit e/32 of qh[e % 32]
+                        lo |= ((h[i] >> (8 * c + 2 * g)) & 1u) << 4;
+                        hi |= ((h[i] >> (8 * c + 2 * g + 1)) & 1u) << 4;
+                    }
+                    a[4 * i + c] = sl * (float)lo;
+                    a[32 + 4 * i + c] = shs * (float)hi;
+                }
+            }
         }
     }
-}
+};
 
-// n consecutive 32-bit words from a 2-byte-aligned address inside a block:
-// aligned loads, realigned by 16 bits when the address is 2 mod 4.  The
-// extra aligned word read stays inside the block for every use below.
-template <int N>
-__device__ __forceinline__ void words_at(const uint8_t* p, uint32_t (&out)[N]) {
-    const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(p) & ~(uintptr_t)3);
-    const uint32_t sh = (reinterpret_cast<uintptr_t>(p) & 2) ? 16u : 0u;
-    uint32_t w[N + 1];
+// acc[i] += the block's contribution to the lane's four outputs
+template <int FMT>
+__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, bool tok_ok, float (&acc)[4]) {
+    float a[64];
+    float m_lo, m_hi;
+    r.codes(g, a, m_lo, m_hi);
+    float xv[64];
 #pragma unroll
-    for (int i = 0; i <= N; ++i) w[i] = a[i];
+    for (int i = 0; i < 16; ++i) {
+        xv[4 * i] = tok_ok ? r.xv[i].x : 0.0f;
+        xv[4 * i + 1] = tok_ok ? r.xv[i].y : 0.0f;
+        xv[4 * i + 2] = tok_ok ? r.xv[i].z : 0.0f;
+        xv[4 * i + 3] = tok_ok ? r.xv[i].w : 0.0f;
+    }
+    f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < N; ++i) out[i] = __builtin_amdgcn_alignbit(w[i + 1], w[i], sh);
-}
-
-// Q6_K: elements 64g..64g+63 are n = g/2, k = 2(g%2) + j/32, l = j%32 of the
-// layout (ql[64n + 32(k%2) + l] nibble k/2, bits 2k..2k+1 of qh[32n + l]),
-// that is bytes j of ql[64n..], nibble g%2, and qh[32n + j%32]; sub-block
-// of 16 is 4g + j/16.
-__device__ __forceinline__ void mm16_group_q6(const uint8_t* blk, int g, float (&a)[64]) {
-    const int n = g >> 1, nib = 4 * (g & 1);
-    uint32_t ql[16], qh[8], scw[1];
-    words_at<16>(blk + 64 * n, ql);
-    words_at<8>(blk + 128 + 32 * n, qh);
-    words_at<1>(blk + 192 + 4 * g, scw);
+    for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
+    if constexpr (FMT == KQ_Q6_K) {
 #pragma unroll
-    for (int j = 0; j < 64; ++j) {
-        const uint32_t lo4 = (ql[j >> 2] >> (8 * (j & 3) + nib)) & 15u;
-        const int k = 2 * (g & 1) + (j >> 5);
-        const uint32_t hb = (qh[(j & 31) >> 2] >> (8 * (j & 3) + 2 * k)) & 3u;
-        const int q = (int)(lo4 | (hb << 4)) - 32;
-        const float sc = (float)(int8_t)(scw[0] >> (8 * (j >> 4)));
-        a[j] = sc * (float)q;
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(r.ohdr[i]), C[i], acc[i]);
+    } else {
+        float slo = 0.0f, shi = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) { slo += xv[j]; shi += xv[32 + j]; }
+        f32x4 C2 = {0.0f, 0.0f, 0.0f, 0.0f};
+        C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_lo, slo, C2, 0, 0, 0);
+        C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_hi, shi, C2, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[i] = __builtin_fmaf(f16_to_f32(r.ohdr[i] & 0xFFFFu), C[i], acc[i]);
+            acc[i] = __builtin_fmaf(-f16_to_f32(r.ohdr[i] >> 16), C2[i], acc[i]);
+        }
     }
 }
 
@@ -1077,44 +1134,26 @@ __global__ __launch_bounds__(64) void kq_matvec16_kernel(const uint8_t* w, int64
 #pragma unroll
     for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int b = 0; b < nb; ++b) {
-        float a[64];
-        float m_lo = 0.0f, m_hi = 0.0f;
-        if constexpr (FMT == KQ_Q6_K) mm16_group_q6(arow + (int64_t)b * BB, g, a);
-        else mm16_group<FMT>(arow + (int64_t)b * BB, g, a, m_lo, m_hi);
-        float xv[64];
-        const float4* xp = reinterpret_cast<const float4*>(xt + 256 * (int64_t)b);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float4 v = xp[i];
-            xv[4 * i] = tok_ok ? v.x : 0.0f;
-            xv[4 * i + 1] = tok_ok ? v.y : 0.0f;
-            xv[4 * i + 2] = tok_ok ? v.z : 0.0f;
-            xv[4 * i + 3] = tok_ok ? v.w : 0.0f;
-        }
-        f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
-        if constexpr (FMT == KQ_Q6_K) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(orow[i] + (int64_t)b * BB + 208));
-                acc[i] = __builtin_fmaf(d, C[i], acc[i]);
-            }
-        } else {
-            float slo = 0.0f, shi = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 32; ++j) { slo += xv[j]; shi += xv[32 + j]; }
-            f32x4 C2 = {0.0f, 0.0f, 0.0f, 0.0f};
-            C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_lo, slo, C2, 0, 0, 0);
-            C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_hi, shi, C2, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t hw = *reinterpret_cast<const uint32_t*>(orow[i] + (int64_t)b * BB);
-                acc[i] = __builtin_fmaf(f16_to_f32(hw & 0xFFFFu), C[i], acc[i]);
-                acc[i] = __builtin_fmaf(-f16_to_f32(hw >> 16), C2[i], acc[i]);
-            }
-        }
+    // two operand sets used in turn; every step reloads one unconditionally
+    // (past the last block it reads the last block again, unused)
+    Mm16Raw<FMT> r0, r1;
+    auto load = [&](Mm16Raw<FMT>& r, int b) {
+        b = min(b, nb - 1);
+        const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
+                                      orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
+        r.load(arow + (int64_t)b * BB, ob, xt + 256 * (int64_t)b, g);
+    };
+    // (the empty asm keeps each set's loads issued where they are written,
+    // ahead of the other set's products, instead of sunk next to their use)
+    load(r0, 0);
+    for (int b = 0; b < nb; b += 2) {
+        load(r1, b + 1);
+        asm volatile("" : : : "memory");
+        mm16_block<FMT>(r0, g, tok_ok, acc);
+        if (b + 1 >= nb) break;
+        load(r0, b + 2);
+        asm volatile("" : : : "memory");
+        mm16_block<FMT>(r1, g, tok_ok, acc);
     }
     if (tok_ok) {
 #pragma unroll
