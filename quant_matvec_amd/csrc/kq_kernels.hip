@@ -1086,17 +1086,19 @@ struct Mm16Raw {
 
 // acc[i] += the block's contribution to the lane's four outputs
 template <int FMT>
-__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, bool tok_ok, float (&acc)[4]) {
+__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
     float a[64];
     float m_lo, m_hi;
     r.codes(g, a, m_lo, m_hi);
+    // a lane past ntok carries the last plane's x: its product column is
+    // never written, and a column of C depends only on its own B column
     float xv[64];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        xv[4 * i] = tok_ok ? r.xv[i].x : 0.0f;
-        xv[4 * i + 1] = tok_ok ? r.xv[i].y : 0.0f;
-        xv[4 * i + 2] = tok_ok ? r.xv[i].z : 0.0f;
-        xv[4 * i + 3] = tok_ok ? r.xv[i].w : 0.0f;
+        xv[4 * i] = r.xv[i].x;
+        xv[4 * i + 1] = r.xv[i].y;
+        xv[4 * i + 2] = r.xv[i].z;
+        xv[4 * i + 3] = r.xv[i].w;
     }
     f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -1119,43 +1121,64 @@ __device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, bool to
     }
 }
 
+// A workgroup of `waves` (1, 2 or 4) waves takes one 16-row tile: wave s
+// walks blocks [s*nb/waves, (s+1)*nb/waves) of it, and wave 0 adds the
+// waves' sums in wave order, so a small matrix still fills the GPU.  The
+// split depends on the matrix alone, never on ntok.
 template <int FMT>
-__global__ __launch_bounds__(64) void kq_matvec16_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows,
-                                                          int32_t nb, const float* x, int64_t ldx, int32_t ntok,
-                                                          float* y, int64_t ldy) {
+__global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows,
+                                                           int32_t nb, const float* x, int64_t ldx, int32_t ntok,
+                                                           float* y, int64_t ldy) {
     constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
-    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    __shared__ float4 part[4][64];
+    const int waves = (int)(blockDim.x >> 6), s = (int)(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
     const int row0 = blockIdx.x * 16;
+    const int b0 = (int)((int64_t)s * nb / waves), b1 = (int)((int64_t)(s + 1) * nb / waves);
     // A rows past the matrix repeat its last row; their results are not written
     const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
-    const bool tok_ok = r16 < ntok;
+    // a lane past ntok reads the last plane's x (its column is not written)
     const float* xt = x + (int64_t)min(r16, ntok - 1) * ldx + 64 * g;
     const uint8_t* orow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    // two operand sets used in turn; every step reloads one unconditionally
-    // (past the last block it reads the last block again, unused)
-    Mm16Raw<FMT> r0, r1;
-    auto load = [&](Mm16Raw<FMT>& r, int b) {
-        b = min(b, nb - 1);
-        const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
-                                      orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
-        r.load(arow + (int64_t)b * BB, ob, xt + 256 * (int64_t)b, g);
-    };
-    // (the empty asm keeps each set's loads issued where they are written,
-    // ahead of the other set's products, instead of sunk next to their use)
-    load(r0, 0);
-    for (int b = 0; b < nb; b += 2) {
-        load(r1, b + 1);
-        asm volatile("" : : : "memory");
-        mm16_block<FMT>(r0, g, tok_ok, acc);
-        if (b + 1 >= nb) break;
-        load(r0, b + 2);
-        asm volatile("" : : : "memory");
-        mm16_block<FMT>(r1, g, tok_ok, acc);
+    if (b0 < b1) {
+        // two operand sets used in turn; every step reloads one
+        // unconditionally (past the last block it reads the last block again,
+        // unused).  The empty asm keeps each set's loads issued where they are
+        // written, ahead of the other set's products, instead of sunk next to
+        // their use.
+        Mm16Raw<FMT> r0, r1;
+        auto load = [&](Mm16Raw<FMT>& r, int b) {
+            b = min(b, b1 - 1);
+            const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
+                                          orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
+            r.load(arow + (int64_t)b * BB, ob, xt + 256 * (int64_t)b, g);
+        };
+        load(r0, b0);
+        for (int b = b0; b < b1; b += 2) {
+            load(r1, b + 1);
+            asm volatile("" : : : "memory");
+            mm16_block<FMT>(r0, g, acc);
+            if (b + 1 >= b1) break;
+            load(r0, b + 2);
+            asm volatile("" : : : "memory");
+            mm16_block<FMT>(r1, g, acc);
+        }
     }
-    if (tok_ok) {
+    if (waves > 1) {
+        part[s][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        __syncthreads();
+        if (s != 0) return;
+        float4 v = part[0][lane];
+        for (int k = 1; k < waves; ++k) {
+            const float4 u = part[k][lane];
+            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
+        }
+        acc[0] = v.x; acc[1] = v.y; acc[2] = v.z; acc[3] = v.w;
+    }
+    if (r16 < ntok) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = row0 + 4 * g + i;
@@ -1168,19 +1191,23 @@ int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, cons
                     int64_t ldy, int32_t ntok, hipStream_t stream) {
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
-    const dim3 grid((unsigned)((rows + 15) / 16));
+    // split the blocks of a tile over 4 / 2 waves while there are at most
+    // 512 / 1024 tiles (the row count alone decides)
+    const int64_t tiles = (rows + 15) / 16;
+    const int waves = tiles <= 512 ? 4 : tiles <= 1024 ? 2 : 1;
+    const dim3 grid((unsigned)tiles), block((unsigned)(64 * waves));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q4_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q4_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
                            ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q5_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q5_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
                            ldx, ntok, y, ldy);
         break;
     default:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
                            ldx, ntok, y, ldy);
         break;
     }
