@@ -70,6 +70,7 @@ enum kq_status {
 #define KQ_MAX_NTOK 8
 #define KQ_MAX_EMBED_IDS (1 << 24)
 #define KQ_MAX_NTOK16 16
+#define KQ_MAX_MATMUL_NTOK (1 << 20)
 
 /* One member of a grid-split set. */
 typedef struct kq_tensor {
@@ -138,6 +139,19 @@ int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok);
 int kq_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols,
                 const float* x, int64_t ldx, float* y, int64_t ldy,
                 int32_t ntok, void* stream);
+
+/*
+ * The same product for a batch of ntok in 1..KQ_MAX_MATMUL_NTOK token planes
+ * (the prefill rung of the batch-width ladder, muser-book Ch 6 Figure 6.7):
+ *   y[t][i] = sum_j W[i,j] x[t][j],  t < ntok,
+ * on the matrix cores, each block decoded once for 64 tokens.  Arguments,
+ * layouts, alignment and errors as kq_matvec16, with ntok up to 2^20.
+ * Results meet the same per-row tolerance; a plane's result does not depend
+ * on ntok or on the other planes.  Allocates nothing.
+ */
+int kq_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols,
+              const float* x, int64_t ldx, float* y, int64_t ldy,
+              int32_t ntok, void* stream);
 
 /*
  * The embedding lookup of muser-book Ch 6 section 6.7: row ids[t] of a Q4_K

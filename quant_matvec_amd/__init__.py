@@ -23,7 +23,7 @@ STATUS = {
     -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE",
 }
 EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set",
-           "kq_matvec16", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
+           "kq_matvec16", "kq_matmul", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
            "kq_version")
 
 
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
         L.kq_dequant.restype = ctypes.c_int
         L.kq_matvec16.argtypes = [i32, vp, i64, i64, vp, i64, vp, i64, i32, vp]
         L.kq_matvec16.restype = ctypes.c_int
+        L.kq_matmul.argtypes = [i32, vp, i64, i64, vp, i64, vp, i64, i32, vp]
+        L.kq_matmul.restype = ctypes.c_int
         L.kq_embed_rows.argtypes = [i32, vp, i64, i64, vp, i32, vp, i64, vp]
         L.kq_embed_rows.restype = ctypes.c_int
         L.kq_debug_read_probe.argtypes = [vp, i64, vp, vp]
@@ -189,6 +191,15 @@ def kq_matvec16(fmt: int, w, rows: int, cols: int, x, y, ntok: int = 16, ldx: in
     ldy = _plane_stride(y, rows) if ldy is None else ldy
     rc = load().kq_matvec16(fmt, _ptr(w), rows, cols, _ptr(x), ldx, _ptr(y), ldy, ntok, _stream(stream))
     _check(rc, "kq_matvec16")
+
+
+def kq_matmul(fmt: int, w, rows: int, cols: int, x, y, ntok: int, ldx: int | None = None,
+              ldy: int | None = None, stream=None) -> None:
+    """y[t][i] = sum_j W[i,j] x[t][j] for a batch of t < ntok planes."""
+    ldx = _plane_stride(x, cols) if ldx is None else ldx
+    ldy = _plane_stride(y, rows) if ldy is None else ldy
+    rc = load().kq_matmul(fmt, _ptr(w), rows, cols, _ptr(x), ldx, _ptr(y), ldy, ntok, _stream(stream))
+    _check(rc, "kq_matmul")
 
 
 def kq_embed_rows(fmt: int, table, rows: int, cols: int, ids, out, ldo: int | None = None,

@@ -21,6 +21,8 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
                  int64_t ldo, hipStream_t stream);
 int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
                     int64_t ldy, int32_t ntok, hipStream_t stream);
+int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+                  int64_t ldy, int32_t ntok, hipStream_t stream);
 
 int32_t block_bytes(int32_t fmt) {
     switch (fmt) {
@@ -339,6 +341,24 @@ int kq_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const fl
     return launch_matvec16(fmt, w, rows, cols, x, ldx, y, ldy, ntok, static_cast<hipStream_t>(stream));
 }
 
+int kq_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+              int64_t ldy, int32_t ntok, void* stream) {
+    kq_tensor t;
+    t.fmt = fmt;
+    t.reserved = 0;
+    t.w = w;
+    t.x = x;
+    t.y = y;
+    t.rows = rows;
+    t.cols = cols;
+    t.ldx = ldx;
+    t.ldy = ldy;
+    const int rc = validate_tensors(&t, 1, ntok, KQ_MAX_MATMUL_NTOK);
+    if (rc != KQ_OK) return rc;
+    if ((rows + 15) / 16 > INT32_MAX) return KQ_ERR_TOO_LARGE;
+    return launch_matmul(fmt, w, rows, cols, x, ldx, y, ldy, ntok, static_cast<hipStream_t>(stream));
+}
+
 int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes_out, int32_t* scales_out,
                      int32_t* mins_out, float* d_out, float* dmin_out, void* stream) {
     if (block_bytes(fmt) < 0) return KQ_ERR_FORMAT;
@@ -397,7 +417,7 @@ const char* kq_strerror(int code) {
     case KQ_ERR_FORMAT: return "unsupported format (only Q4_K=12, Q5_K=13, Q6_K=14)";
     case KQ_ERR_COLS: return "cols must be a positive multiple of 256";
     case KQ_ERR_ROWS: return "rows (or block count) must be positive";
-    case KQ_ERR_NTOK: return "ntok must be in 1..8 (1..16 for kq_matvec16)";
+    case KQ_ERR_NTOK: return "ntok must be in 1..8 (1..16 for kq_matvec16, 1..2^20 for kq_matmul)";
     case KQ_ERR_NULL: return "null pointer";
     case KQ_ERR_ALIGN: return "misaligned pointer (w, x need 16 bytes; y 4 bytes)";
     case KQ_ERR_STRIDE: return "bad leading dimension (ldx >= cols and a multiple of 4; ldy >= rows)";

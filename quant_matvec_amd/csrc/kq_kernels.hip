@@ -995,7 +995,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // its token's x over the same 64 elements, and the headers of the block in
 // its four output rows.  Loads and use are split so that the next block's
 // loads are in flight while this block's products run.
-template <int FMT>
+template <int FMT, bool WITHX = true>
 struct Mm16Raw {
     uint4 hdr, q0, q1, h0, h1;        // Q4_K/Q5_K (h0, h1: Q5_K qh)
     uint32_t ql[17], qh[9], scw[2];   // Q6_K aligned words
@@ -1032,9 +1032,11 @@ struct Mm16Raw {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint32_t*>(oblk[i]);
         }
-        const float4* xp = reinterpret_cast<const float4*>(xb);
+        if constexpr (WITHX) {
+            const float4* xp = reinterpret_cast<const float4*>(xb);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xv[i] = xp[i];
+            for (int i = 0; i < 16; ++i) xv[i] = xp[i];
+        }
     }
 
     // sc*q of elements 64g..64g+63 in element order, and (Q4_K/Q5_K) the
@@ -1084,28 +1086,28 @@ struct Mm16Raw {
     }
 };
 
-// acc[i] += the block's contribution to the lane's four outputs
+// acc[i] += one block's contribution to the lane's four outputs, from the
+// block's sc*q values a, mins and row headers, and one 16-token tile of x
 template <int FMT>
-__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
-    float a[64];
-    float m_lo, m_hi;
-    r.codes(g, a, m_lo, m_hi);
+__device__ __forceinline__ void mm16_products(const float (&a)[64], float m_lo, float m_hi,
+                                              const uint32_t (&ohdr)[4], const float4 (&x4)[16], float (&acc)[4]) {
     // a lane past ntok carries the last plane's x: its product column is
     // never written, and a column of C depends only on its own B column
     float xv[64];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        xv[4 * i] = r.xv[i].x;
-        xv[4 * i + 1] = r.xv[i].y;
-        xv[4 * i + 2] = r.xv[i].z;
-        xv[4 * i + 3] = r.xv[i].w;
+        xv[4 * i] = x4[i].x;
+        xv[4 * i + 1] = x4[i].y;
+        xv[4 * i + 2] = x4[i].z;
+        xv[4 * i + 3] = x4[i].w;
     }
     f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
     if constexpr (FMT == KQ_Q6_K) {
+        (void)m_lo; (void)m_hi;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(r.ohdr[i]), C[i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i]), C[i], acc[i]);
     } else {
         float slo = 0.0f, shi = 0.0f;
 #pragma unroll
@@ -1115,10 +1117,18 @@ __device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (
         C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_hi, shi, C2, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            acc[i] = __builtin_fmaf(f16_to_f32(r.ohdr[i] & 0xFFFFu), C[i], acc[i]);
-            acc[i] = __builtin_fmaf(-f16_to_f32(r.ohdr[i] >> 16), C2[i], acc[i]);
+            acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i] & 0xFFFFu), C[i], acc[i]);
+            acc[i] = __builtin_fmaf(-f16_to_f32(ohdr[i] >> 16), C2[i], acc[i]);
         }
     }
+}
+
+template <int FMT>
+__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
+    float a[64];
+    float m_lo, m_hi;
+    r.codes(g, a, m_lo, m_hi);
+    mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, r.xv, acc);
 }
 
 // A workgroup of `waves` (1, 2 or 4) waves takes one 16-row tile: wave s
@@ -1185,6 +1195,101 @@ __global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int6
             if (r < rows) y[(int64_t)r16 * ldy + r] = acc[i];
         }
     }
+}
+
+// Many token planes (a prefill batch): the same 16-row tile and products,
+// with each block's sc*q decoded once and used for TT tiles of 16 tokens
+// (the pages' mul_mm rung, Ch 6 Figure 6.7, decodes a block once for a whole
+// tile of tokens too).  Workgroup (row tile, token group) = (blockIdx.x,
+// blockIdx.y); the x of the next 16-token tile is loaded while the current
+// one's products run.  A plane's result does not depend on ntok or on the
+// other planes.
+template <int FMT, int TT>
+__global__ __launch_bounds__(64) void kq_matmul_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
+                                                       const float* x, int64_t ldx, int32_t ntok, float* y,
+                                                       int64_t ldy) {
+    constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
+    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    const int row0 = blockIdx.x * 16;
+    const int tok0 = blockIdx.y * 16 * TT;
+    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
+    const uint8_t* orow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
+    // lane's token in each tile (past ntok: the last plane, never written)
+    const float* xt[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) xt[t] = x + (int64_t)min(tok0 + 16 * t + r16, ntok - 1) * ldx + 64 * g;
+    float acc[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
+    for (int b = 0; b < nb; ++b) {
+        Mm16Raw<FMT, false> r;
+        const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
+                                      orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
+        r.load(arow + (int64_t)b * BB, ob, nullptr, g);
+        float4 xa[16], xb[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xa[i] = reinterpret_cast<const float4*>(xt[0] + 256 * (int64_t)b)[i];
+        float a[64];
+        float m_lo, m_hi;
+        r.codes(g, a, m_lo, m_hi);
+#pragma unroll
+        for (int t = 0; t < TT; t += 2) {
+            if (t + 1 < TT) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) xb[i] = reinterpret_cast<const float4*>(xt[t + 1] + 256 * (int64_t)b)[i];
+                asm volatile("" : : : "memory");
+            }
+            mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, xa, acc[t]);
+            if (t + 1 < TT) {
+                if (t + 2 < TT) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        xa[i] = reinterpret_cast<const float4*>(xt[t + 2] + 256 * (int64_t)b)[i];
+                    asm volatile("" : : : "memory");
+                }
+                mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, xb, acc[t + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        const int tok = tok0 + 16 * t + r16;
+        if (tok < ntok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = row0 + 4 * g + i;
+                if (r < rows) y[(int64_t)tok * ldy + r] = acc[t][i];
+            }
+        }
+    }
+}
+
+int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
+                  int64_t ldy, int32_t ntok, hipStream_t stream) {
+    constexpr int TT = 4;                       // 64 tokens a workgroup
+    const int32_t nb = (int32_t)(cols / 256);
+    const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
+    const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((ntok + 16 * TT - 1) / (16 * TT)));
+    const uint8_t* wb = static_cast<const uint8_t*>(w);
+    switch (fmt) {
+    case KQ_Q4_K:
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
+        break;
+    case KQ_Q5_K:
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
+        break;
+    default:
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
+        break;
+    }
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
 int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,

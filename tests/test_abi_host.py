@@ -178,3 +178,16 @@ def test_matvec16_admission(lib):
     assert lib.kq_matvec16(12, W, 256, 6656, X, 6654, Y, 256, 16, None) == -7
     # y planes reaching into x
     assert lib.kq_matvec16(12, W, 256, 6656, X, 6656, X - 4096, 256, 16, None) == -8
+
+
+def test_matmul_admission(lib):
+    """kq_matmul takes 1..2^20 token planes and otherwise the checks of
+    kq_matvec, all on the host."""
+    W, X, Y = BASE, BASE + (1 << 36), BASE + (2 << 36)
+    assert lib.kq_matmul(12, W, 256, 6656, X, 6656, Y, 256, 0, None) == -4
+    assert lib.kq_matmul(12, W, 256, 6656, X, 6656, Y, 256, (1 << 20) + 1, None) == -4
+    assert lib.kq_matmul(9, W, 256, 6656, X, 6656, Y, 256, 512, None) == -1
+    assert lib.kq_matmul(12, W, 256, 6656, X + 8, 6656, Y, 256, 512, None) == -6
+    assert lib.kq_matmul(12, W, 256, 6656, X, 6656, Y, 255, 512, None) == -7
+    # 512 planes of y reaching into x
+    assert lib.kq_matmul(12, W, 256, 6656, X, 6656, X - 512 * 256 * 4 + 1024, 256, 512, None) == -8

@@ -495,3 +495,56 @@ def test_matvec16_release_shapes_sampled():
         idx = _sample_rows(T.rows, 60, tile=16)[:700]
         y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, row_idx=idx, nthreads=8)
         check_tol(y[:, idx], y_ref, s, "matvec16 " + T.name)
+
+
+# ---- a prefill batch (kq_matmul): any number of token planes, each block
+# decoded once for 64 tokens (the mul_mm rung of Ch 6 Figure 6.7).
+
+def _gpu_matmul(fmt, w_np, rows, cols, x_np, ldy=None):
+    t = torch()
+    x_np = np.atleast_2d(x_np).astype(np.float32)
+    ntok = x_np.shape[0]
+    ldy = ldy or rows
+    y = t.full((ntok, ldy), float("nan"), dtype=t.float32, device="cuda")
+    kq.kq_matmul(fmt, dev(w_np.reshape(-1)), rows, cols, dev(x_np), y, ntok=ntok, ldy=ldy)
+    out = host(y)
+    if ldy > rows:
+        assert np.isnan(out[:, rows:]).all(), "kernel wrote past rows"
+    return out[:, :rows]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 17), (300, 2560, 64), (100, 6656, 130), (16, 256, 1)])
+def test_matmul_parity(fmt, rows, cols, ntok):
+    w = kqgen.weights(fmt, rows, cols, 810, fmt, rows, cols)
+    x = kqgen.activations(ntok, cols, 811, ntok, cols)
+    note("matmul fmt=%d %dx%d ntok=%d" % (fmt, rows, cols, ntok))
+    y = _gpu_matmul(fmt, w, rows, cols, x, ldy=rows + 3)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=8)
+    check_tol(y, y_ref, s, "matmul fmt %d %dx%d ntok %d" % (fmt, rows, cols, ntok))
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_matmul_plane_independent_of_ntok(fmt):
+    rows, cols = 70, 1024
+    w = kqgen.weights(fmt, rows, cols, 812, fmt)
+    x = kqgen.activations(130, cols, 813, fmt)
+    note("matmul planes fmt=%d" % fmt)
+    y = _gpu_matmul(fmt, w, rows, cols, x)
+    for n in (1, 64, 65):
+        yn = _gpu_matmul(fmt, w, rows, cols, x[:n])
+        assert np.array_equal(yn.view(np.uint32), y[:n].view(np.uint32)), n
+
+
+def test_matmul_prefill_sampled():
+    """A 512-token prefill batch through the FFN gate (19968 x 6656 Q4_K)
+    and the Q6_K FFN down (6656 x 19968), rows sampled."""
+    for launch in (wl.ffn_gate_up(layer=0), wl.ffn_down(layer=1)):
+        T = launch[0][0]
+        w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+        x = kqgen.activations(512, T.cols, 814, T.cols)
+        note("matmul prefill %s fmt=%d %dx%d ntok=512" % (T.name, T.fmt, T.rows, T.cols))
+        y = _gpu_matmul(T.fmt, w, T.rows, T.cols, x)
+        idx = _sample_rows(T.rows, 61, tile=16)[:300]
+        y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, row_idx=idx, nthreads=8)
+        check_tol(y[:, idx], y_ref, s, "matmul prefill " + T.name)
