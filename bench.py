@@ -269,6 +269,8 @@ def other_configs(dev):
     torch.cuda.empty_cache()
     res.update(matvec16_configs(dev))
     torch.cuda.empty_cache()
+    res.update(matmul_configs(dev))
+    torch.cuda.empty_cache()
     # calibration: the library's trivial 16-byte streaming-read probe over 2 GiB
     import quant_matvec_amd as kq
     buf = torch.ones(1 << 29, dtype=torch.float32, device=dev)
@@ -342,6 +344,44 @@ def matvec16_configs(dev):
                 "weight_GBs": round(wbytes / len(mem) / (us * 1e-6) / 1e9, 1),
                 "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2)}
         del mem
+        torch.cuda.empty_cache()
+    return out_res
+
+
+def matmul_configs(dev):
+    """A 512-token prefill batch (kq_matmul) through release shapes: fp32
+    matrix-core flops (2 a weight a token) per second."""
+    import torch
+
+    import kqgen
+    import quant_matvec_amd as kq
+    from kqgen import workloads as wl
+
+    out_res = {}
+    stream = torch.cuda.current_stream()
+    ntok = 512
+    for name, T, reps in (("attn_output_q4k", wl.attn_output()[0][0], 20),
+                          ("ffn_gate_q4k", wl.ffn_gate_up()[0][0], 5),
+                          ("ffn_down_q6k", wl.ffn_down(layer=1)[0][0], 5)):
+        print("[bench] generating %s for a prefill batch" % name, file=sys.stderr, flush=True)
+        w = torch.from_numpy(kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey).reshape(-1)).to(dev)
+        x = torch.from_numpy(kqgen.activations(ntok, T.cols, *T.xkey)).to(dev)
+        y = torch.empty((ntok, T.rows), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            kq.kq_matmul(T.fmt, w, T.rows, T.cols, x, y, ntok=ntok, stream=stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            kq.kq_matmul(T.fmt, w, T.rows, T.cols, x, y, ntok=ntok, stream=stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = 2 * ntok * T.rows * T.cols / (us * 1e-6) / 1e12
+        out_res["F4_prefill512_%s" % name] = {"workload": "%s_%dx%d_ntok%d" % (name, T.rows, T.cols, ntok),
+                                              "us_per_call": round(us, 1), "TFLOPs": round(tf, 2),
+                                              "fp32_matrix_peak_frac": round(tf / 157.3, 4)}
+        del w, x, y
         torch.cuda.empty_cache()
     return out_res
 
