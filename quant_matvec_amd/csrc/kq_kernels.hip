@@ -1197,72 +1197,89 @@ __global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int6
     }
 }
 
-// Many token planes (a prefill batch): the same 16-row tile and products,
-// with each block's sc*q decoded once and used for TT tiles of 16 tokens
-// (the pages' mul_mm rung, Ch 6 Figure 6.7, decodes a block once for a whole
-// tile of tokens too).  Workgroup (row tile, token group) = (blockIdx.x,
-// blockIdx.y); the x of the next 16-token tile is loaded while the current
-// one's products run.  A plane's result does not depend on ntok or on the
-// other planes.
-template <int FMT, int TT>
-__global__ __launch_bounds__(64) void kq_matmul_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
-                                                       const float* x, int64_t ldx, int32_t ntok, float* y,
-                                                       int64_t ldy) {
+// Many token planes (a prefill batch): the same 16-row tile and products.
+// A workgroup of four waves takes four row tiles and 64 tokens, so every
+// block's x (64 tokens x 256 floats) is shared by the four waves through
+// LDS: the workgroup loads it once with coalesced 16-byte loads (a token's
+// 1 KB by 64 consecutive lanes), and each wave reads its product operands
+// from LDS for each of its four 16-token tiles.  Each block's sc*q values
+// are decoded once per wave and used for all four tiles.  The next block's
+// x and weights are loaded into registers while this block's products run.
+// Token rows in LDS are 1040 bytes apart, so the 16 lanes of a 16-byte LDS
+// read (one per token) fall on distinct banks.  A plane's result does not
+// depend on ntok or on the other planes.
+constexpr int kMmTok = 64;                 // tokens a workgroup
+constexpr int kMmXRow = 1040;              // LDS bytes a token row (1024 + 16)
+
+template <int FMT>
+__global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
+                                                        const float* x, int64_t ldx, int32_t ntok, float* y,
+                                                        int64_t ldy) {
     constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
-    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
-    const int row0 = blockIdx.x * 16;
-    const int tok0 = blockIdx.y * 16 * TT;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kMmTok * kMmXRow];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+    const int row0 = (blockIdx.x * 4 + wave) * 16;
+    const int tok0 = blockIdx.y * kMmTok;
+    // rows past the matrix repeat its last row; their results are not written
     const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
     const uint8_t* orow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
-    // lane's token in each tile (past ntok: the last plane, never written)
-    const float* xt[TT];
+    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i < 16
+    // (tokens past ntok repeat the last plane; their columns are not written)
+    const float* xcol = x + 4 * (tid & 63);
+    const int xtok = tok0 + (tid >> 6);
+    float acc[4][4];
 #pragma unroll
-    for (int t = 0; t < TT; ++t) xt[t] = x + (int64_t)min(tok0 + 16 * t + r16, ntok - 1) * ldx + 64 * g;
-    float acc[TT][4];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
+    u32x4 xr[16];
+    Mm16Raw<FMT, false> r;
+    // every step loads the next block unconditionally (past the last block
+    // it loads the last one again, unused)
+#define KQ_MM_LOAD(b_)                                                                                     \
+    {                                                                                                      \
+        const int64_t bo_ = (int64_t)(b_) * BB;                                                            \
+        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                                     \
+            xr[i] = *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + 4 * i, ntok - 1) * ldx +     \
+                                                    256 * (int64_t)(b_));                                  \
+        const uint8_t* const ob_[4] = {orow[0] + bo_, orow[1] + bo_, orow[2] + bo_, orow[3] + bo_};        \
+        r.load(arow + bo_, ob_, nullptr, g);                                                               \
+    }
+    KQ_MM_LOAD(0)
     for (int b = 0; b < nb; ++b) {
-        Mm16Raw<FMT, false> r;
-        const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
-                                      orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
-        r.load(arow + (int64_t)b * BB, ob, nullptr, g);
-        float4 xa[16], xb[16];
+        __syncthreads();                                    // the previous block's LDS reads are done
 #pragma unroll
-        for (int i = 0; i < 16; ++i) xa[i] = reinterpret_cast<const float4*>(xt[0] + 256 * (int64_t)b)[i];
+        for (int i = 0; i < 16; ++i)
+            *reinterpret_cast<u32x4*>(xs + ((tid >> 6) + 4 * i) * kMmXRow + 16 * (tid & 63)) = xr[i];
         float a[64];
         float m_lo, m_hi;
         r.codes(g, a, m_lo, m_hi);
+        uint32_t oh[4];
 #pragma unroll
-        for (int t = 0; t < TT; t += 2) {
-            if (t + 1 < TT) {
+        for (int i = 0; i < 4; ++i) oh[i] = r.ohdr[i];
+        __syncthreads();                                    // x of block b is in LDS
+        KQ_MM_LOAD(min(b + 1, nb - 1))
+        asm volatile("" : : : "memory");
 #pragma unroll
-                for (int i = 0; i < 16; ++i) xb[i] = reinterpret_cast<const float4*>(xt[t + 1] + 256 * (int64_t)b)[i];
-                asm volatile("" : : : "memory");
-            }
-            mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, xa, acc[t]);
-            if (t + 1 < TT) {
-                if (t + 2 < TT) {
+        for (int t = 0; t < 4; ++t) {
+            float4 x4[16];
+            const uint8_t* src = xs + (16 * t + r16) * kMmXRow + 256 * g;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        xa[i] = reinterpret_cast<const float4*>(xt[t + 2] + 256 * (int64_t)b)[i];
-                    asm volatile("" : : : "memory");
-                }
-                mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, xb, acc[t + 1]);
-            }
+            for (int i = 0; i < 16; ++i) x4[i] = *reinterpret_cast<const float4*>(src + 16 * i);
+            mm16_products<FMT>(a, m_lo, m_hi, oh, x4, acc[t]);
         }
     }
+#undef KQ_MM_LOAD
 #pragma unroll
-    for (int t = 0; t < TT; ++t) {
+    for (int t = 0; t < 4; ++t) {
         const int tok = tok0 + 16 * t + r16;
         if (tok < ntok) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = row0 + 4 * g + i;
-                if (r < rows) y[(int64_t)tok * ldy + r] = acc[t][i];
+                const int rr = row0 + 4 * g + i;
+                if (rr < rows) y[(int64_t)tok * ldy + rr] = acc[t][i];
             }
         }
     }
@@ -1270,23 +1287,22 @@ __global__ __launch_bounds__(64) void kq_matmul_kernel(const uint8_t* w, int64_t
 
 int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
                   int64_t ldy, int32_t ntok, hipStream_t stream) {
-    constexpr int TT = 4;                       // 64 tokens a workgroup
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
-    const dim3 grid((unsigned)((rows + 15) / 16), (unsigned)((ntok + 16 * TT - 1) / (16 * TT)));
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + kMmTok - 1) / kMmTok));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
-                           nb, x, ldx, ntok, y, ldy);
+        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q4_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
-                           nb, x, ldx, ntok, y, ldy);
+        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q5_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
         break;
     default:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, TT>), grid, dim3(64), 0, stream, wb, row_bytes, (int32_t)rows,
-                           nb, x, ldx, ntok, y, ldy);
+        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q6_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                           ldx, ntok, y, ldy);
         break;
     }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
