@@ -1198,50 +1198,52 @@ __global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int6
 }
 
 // Many token planes (a prefill batch): the same 16-row tile and products.
-// A workgroup of four waves takes four row tiles and 64 tokens, so every
-// block's x (64 tokens x 256 floats) is shared by the four waves through
+// A workgroup of four waves takes four row tiles and 16*TT tokens (TT = 4:
+// 64 tokens; TT = 1 serves the 16-plane call on large matrices), so every
+// block's x (16*TT tokens x 256 floats) is shared by the four waves through
 // LDS: the workgroup loads it once with coalesced 16-byte loads (a token's
 // 1 KB by 64 consecutive lanes), and each wave reads its product operands
-// from LDS for each of its four 16-token tiles.  Each block's sc*q values
-// are decoded once per wave and used for all four tiles.  The next block's
+// from LDS for each of its TT 16-token tiles.  Each block's sc*q values
+// are decoded once per wave and used for all TT tiles.  The next block's
 // x and weights are loaded into registers while this block's products run.
 // Token rows in LDS are 1040 bytes apart, so the 16 lanes of a 16-byte LDS
 // read (one per token) fall on distinct banks.  A plane's result does not
 // depend on ntok or on the other planes.
-constexpr int kMmTok = 64;                 // tokens a workgroup
 constexpr int kMmXRow = 1040;              // LDS bytes a token row (1024 + 16)
 
-template <int FMT>
+template <int FMT, int TT>
 __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
                                                         const float* x, int64_t ldx, int32_t ntok, float* y,
                                                         int64_t ldy) {
     constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
-    __shared__ __attribute__((aligned(16))) uint8_t xs[kMmTok * kMmXRow];
+    constexpr int kTok = 16 * TT;          // tokens a workgroup
+    constexpr int kXR = 4 * TT;            // 16-byte x pieces a thread stages per block
+    __shared__ __attribute__((aligned(16))) uint8_t xs[kTok * kMmXRow];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
     const int row0 = (blockIdx.x * 4 + wave) * 16;
-    const int tok0 = blockIdx.y * kMmTok;
+    const int tok0 = blockIdx.y * kTok;
     // rows past the matrix repeat its last row; their results are not written
     const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
     const uint8_t* orow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
-    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i < 16
+    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i < 4*TT
     // (tokens past ntok repeat the last plane; their columns are not written)
     const float* xcol = x + 4 * (tid & 63);
     const int xtok = tok0 + (tid >> 6);
-    float acc[4][4];
+    float acc[TT][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-    u32x4 xr[16];
+    u32x4 xr[kXR];
     Mm16Raw<FMT, false> r;
     // every step loads the next block unconditionally (past the last block
     // it loads the last one again, unused)
 #define KQ_MM_LOAD(b_)                                                                                     \
     {                                                                                                      \
         const int64_t bo_ = (int64_t)(b_) * BB;                                                            \
-        _Pragma("unroll") for (int i = 0; i < 16; ++i)                                                     \
+        _Pragma("unroll") for (int i = 0; i < kXR; ++i)                                                    \
             xr[i] = *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + 4 * i, ntok - 1) * ldx +     \
                                                     256 * (int64_t)(b_));                                  \
         const uint8_t* const ob_[4] = {orow[0] + bo_, orow[1] + bo_, orow[2] + bo_, orow[3] + bo_};        \
@@ -1251,7 +1253,7 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
     for (int b = 0; b < nb; ++b) {
         __syncthreads();                                    // the previous block's LDS reads are done
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
+        for (int i = 0; i < kXR; ++i)
             *reinterpret_cast<u32x4*>(xs + ((tid >> 6) + 4 * i) * kMmXRow + 16 * (tid & 63)) = xr[i];
         float a[64];
         float m_lo, m_hi;
@@ -1263,7 +1265,7 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
         KQ_MM_LOAD(min(b + 1, nb - 1))
         asm volatile("" : : : "memory");
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < TT; ++t) {
             float4 x4[16];
             const uint8_t* src = xs + (16 * t + r16) * kMmXRow + 256 * g;
 #pragma unroll
@@ -1273,7 +1275,7 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
     }
 #undef KQ_MM_LOAD
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < TT; ++t) {
         const int tok = tok0 + 16 * t + r16;
         if (tok < ntok) {
 #pragma unroll
@@ -1289,20 +1291,20 @@ int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const 
                   int64_t ldy, int32_t ntok, hipStream_t stream) {
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
-    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + kMmTok - 1) / kMmTok));
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + 63) / 64));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q4_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q5_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
         break;
     default:
-        hipLaunchKernelGGL(kq_matmul_kernel<KQ_Q6_K>, grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
         break;
     }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
@@ -1313,11 +1315,30 @@ int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, cons
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
     // split the blocks of a tile over 4 / 2 waves while there are at most
-    // 512 / 1024 tiles (the row count alone decides)
+    // 512 / 1024 tiles (the row count alone decides); beyond that, four row
+    // tiles a workgroup share x through LDS (the same products per output)
     const int64_t tiles = (rows + 15) / 16;
     const int waves = tiles <= 512 ? 4 : tiles <= 1024 ? 2 : 1;
     const dim3 grid((unsigned)tiles), block((unsigned)(64 * waves));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
+    if (waves == 1) {
+        const dim3 g4((unsigned)((rows + 63) / 64));
+        switch (fmt) {
+        case KQ_Q4_K:
+            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
+                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
+            break;
+        case KQ_Q5_K:
+            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
+                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
+            break;
+        default:
+            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
+                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
+            break;
+        }
+        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+    }
     switch (fmt) {
     case KQ_Q4_K:
         hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q4_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,

@@ -458,7 +458,7 @@ def _gpu_matvec16(fmt, w_np, rows, cols, x_np, ldy=None):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 16), (300, 6656, 16), (4100, 2560, 9), (16, 256, 1),
-                                            (1, 512, 16)])
+                                            (1, 512, 16), (16400, 768, 16), (16420, 512, 3)])
 def test_matvec16_parity(fmt, rows, cols, ntok):
     w = kqgen.weights(fmt, rows, cols, 800, fmt, rows, cols)
     x = kqgen.activations(ntok, cols, 801, ntok, cols)
@@ -473,14 +473,14 @@ def test_matvec16_parity(fmt, rows, cols, ntok):
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_matvec16_plane_independent_of_ntok(fmt):
     """A token plane's result is bitwise the same whatever ntok is."""
-    rows, cols = 200, 1536
-    w = kqgen.weights(fmt, rows, cols, 802, fmt)
-    x = kqgen.activations(16, cols, 803, fmt)
-    note("matvec16 planes fmt=%d" % fmt)
-    y16 = _gpu_matvec16(fmt, w, rows, cols, x)
-    for n in (1, 5, 11):
-        yn = _gpu_matvec16(fmt, w, rows, cols, x[:n])
-        assert np.array_equal(yn.view(np.uint32), y16[:n].view(np.uint32)), n
+    for rows, cols in ((200, 1536), (16420, 512)):     # split tiles; shared-x tiles
+        w = kqgen.weights(fmt, rows, cols, 802, fmt)
+        x = kqgen.activations(16, cols, 803, fmt)
+        note("matvec16 planes fmt=%d rows=%d" % (fmt, rows))
+        y16 = _gpu_matvec16(fmt, w, rows, cols, x)
+        for n in (1, 5, 11):
+            yn = _gpu_matvec16(fmt, w, rows, cols, x[:n])
+            assert np.array_equal(yn.view(np.uint32), y16[:n].view(np.uint32)), n
 
 
 def test_matvec16_release_shapes_sampled():
