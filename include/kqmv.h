@@ -144,7 +144,7 @@ int kq_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols,
  * The same product for a batch of ntok in 1..KQ_MAX_MATMUL_NTOK token planes
  * (the prefill rung of the batch-width ladder, muser-book Ch 6 Figure 6.7):
  *   y[t][i] = sum_j W[i,j] x[t][j],  t < ntok,
- * on the matrix cores, each block decoded once for 64 tokens.  Arguments,
+ * on the matrix cores, each block decoded once for 32 tokens.  Arguments,
  * layouts, alignment and errors as kq_matvec16, with ntok up to 2^20.
  * Results meet the same per-row tolerance; a plane's result does not depend
  * on ntok or on the other planes.  Allocates nothing.

@@ -1198,8 +1198,8 @@ __global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int6
 }
 
 // Many token planes (a prefill batch): the same 16-row tile and products.
-// A workgroup of four waves takes four row tiles and 16*TT tokens (TT = 4:
-// 64 tokens; TT = 1 serves the 16-plane call on large matrices), so every
+// A workgroup of four waves takes four row tiles and 16*TT tokens (TT = 2
+// for a batch; TT = 1 serves the 16-plane call on large matrices), so every
 // block's x (16*TT tokens x 256 floats) is shared by the four waves through
 // LDS: the workgroup loads it once with coalesced 16-byte loads (a token's
 // 1 KB by 64 consecutive lanes), and each wave reads its product operands
@@ -1291,19 +1291,22 @@ int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const 
                   int64_t ldy, int32_t ntok, hipStream_t stream) {
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
-    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + 63) / 64));
+    // 32 tokens a workgroup: two 16-token tiles (four tiles need more
+    // accumulator and staging registers than fit two waves a SIMD, and ran
+    // slower)
+    const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + 31) / 32));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     default:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 4>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     }

@@ -498,7 +498,7 @@ def test_matvec16_release_shapes_sampled():
 
 
 # ---- a prefill batch (kq_matmul): any number of token planes, each block
-# decoded once for 64 tokens (the mul_mm rung of Ch 6 Figure 6.7).
+# decoded once for 32 tokens (the mul_mm rung of Ch 6 Figure 6.7).
 
 def _gpu_matmul(fmt, w_np, rows, cols, x_np, ldy=None):
     t = torch()
