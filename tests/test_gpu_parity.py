@@ -548,3 +548,24 @@ def test_matmul_prefill_sampled():
         idx = _sample_rows(T.rows, 61, tile=16)[:300]
         y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, row_idx=idx, nthreads=8)
         check_tol(y[:, idx], y_ref, s, "matmul prefill " + T.name)
+
+
+@pytest.mark.parametrize("entry", ["kq_matvec16", "kq_matmul"])
+def test_matrix_core_paths_strided_planes(entry):
+    """Padded x and y planes (ldx > cols, ldy > rows) through the
+    matrix-core entry points: the padding is neither read into the result
+    nor written."""
+    t = torch()
+    fmt, rows, cols, ntok = Q4_K, 70, 1024, 12
+    ldx, ldy = cols + 20, rows + 9
+    w = kqgen.weights(fmt, rows, cols, 820, ntok)
+    x = kqgen.activations(ntok, cols, 821, ntok)
+    xp = np.full((ntok, ldx), np.nan, np.float32)
+    xp[:, :cols] = x
+    y = t.full((ntok, ldy), -3.0, dtype=t.float32, device="cuda")
+    note("%s strided planes" % entry)
+    getattr(kq, entry)(fmt, dev(w.reshape(-1)), rows, cols, dev(xp), y, ntok=ntok, ldx=ldx, ldy=ldy)
+    yh = host(y)
+    assert (yh[:, rows:] == -3.0).all()
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
+    check_tol(yh[:, :rows], y_ref, s, entry + " strided")
