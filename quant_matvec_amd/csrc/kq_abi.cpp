@@ -43,20 +43,23 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
     return w + 1024 * ntok * (pair ? 2 : 1);
 }
 
-// Segment length S: 2 super-blocks (18-27 KB per 64-row segment), except
-// for matrices whose workgroups get few segments in any launch: Q6_K
-// matrices of at most kSmallRows rows and any matrix of at most kTinyRows
-// rows take 1.  A decode set then splits into runs of similar size (its
-// small Q6_K K and V would otherwise be the longest runs), a K/V-sized
-// launch into one-block runs, while a large matrix keeps few partial sums.
-// Depends on (fmt, rows, cols) only.
+// Segment length S: 2 super-blocks, except for matrices whose workgroups
+// get few segments in any launch: any matrix of at most kTinyRows rows, and
+// a Q6_K matrix of at most kSmallRows rows with an odd number of blocks a
+// row, take 1.  A K/V-sized launch then splits into one-block runs, a
+// decode set into runs of similar size, while a large matrix keeps few
+// partial sums.  Depends on (fmt, rows, cols) only, never on ntok.
 //
-// Tile rows: 32 for a matrix of more than kSmallRows rows and an even number
-// of blocks a row, else 64.  With 64-row tiles every wave of an XCD keeps the
-// L2 lines its 64 rows share between successive block columns live, more
-// than the L2 holds on a large matrix, and about a third of the lines are
-// read twice; 32-row tiles that take a segment (two columns) a step halve
-// that and stay near one read per line.
+// Tile rows: 32 for a matrix of more than kTinyRows rows and an even number
+// of blocks a row at one token plane (and at two up to kSmallRows rows),
+// else 64.  With 64-row tiles every wave of an XCD keeps the L2 lines its 64
+// rows share between successive block columns live, more than the L2 holds
+// on a large matrix, and about a third of the lines are read twice; 32-row
+// tiles that take a segment (two columns) a step halve that and stay near
+// one read per line, and give a decode set twice as many, shorter segments.
+// With more token planes the compute per byte grows and 64-row tiles are
+// faster.  Both heights sum the same two-block segments the same way, so a
+// plane's result does not depend on the height.
 constexpr int64_t kSmallRows = 16384;
 constexpr int64_t kTinyRows = 1024;
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
