@@ -342,7 +342,8 @@ def matvec16_configs(dev):
             out_res["F2_%s_ntok16_%s" % (name, key)] = {
                 "workload": "%s_ntok16" % name, "entry": key, "us_per_tensor": round(us, 3),
                 "weight_GBs": round(wbytes / len(mem) / (us * 1e-6) / 1e9, 1),
-                "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2)}
+                "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2),
+                "fp32_matrix_peak_frac": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12 / 157.3, 4)}
         del mem
         torch.cuda.empty_cache()
     return out_res
