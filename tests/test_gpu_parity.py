@@ -1,7 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle.
 
-Integer decode (codes, scales, mins, headers) and the dequantized float32
-weights are compared bit for bit; matvec outputs per row against the
+Integer decode (codes, scales, mins, headers), the dequantized float32
+weights and the embedding rows are compared bit for bit; matvec outputs
+(kq_matvec, kq_matvec_set, kq_matvec16, kq_matmul) per row against the
 binary64 oracle with |y_gpu - y_ref| <= 1e-4 * sum_j|W_ij x_j| + 1e-6.
 Inputs are the seeded synthetic blocks of kqgen.
 """
