@@ -515,7 +515,8 @@ def _gpu_matmul(fmt, w_np, rows, cols, x_np, ldy=None):
 
 
 @pytest.mark.parametrize("fmt", FORMATS)
-@pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 17), (300, 2560, 64), (100, 6656, 130), (16, 256, 1)])
+@pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 17), (300, 2560, 64), (100, 6656, 130), (16, 256, 1),
+                                            (1, 256, 40), (5, 512, 33)])
 def test_matmul_parity(fmt, rows, cols, ntok):
     w = kqgen.weights(fmt, rows, cols, 810, fmt, rows, cols)
     x = kqgen.activations(ntok, cols, 811, ntok, cols)
