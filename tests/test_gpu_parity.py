@@ -571,3 +571,27 @@ def test_matrix_core_paths_strided_planes(entry):
     assert (yh[:, rows:] == -3.0).all()
     y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
     check_tol(yh[:, :rows], y_ref, s, entry + " strided")
+
+
+def test_random_shapes_every_entry_point():
+    """Seeded random shapes (ragged rows, odd and even block counts, any
+    plane count) through kq_matvec, kq_matvec16 and kq_matmul against the
+    oracle."""
+    rng = np.random.default_rng(2026)
+    for case in range(18):
+        fmt = int(rng.choice(FORMATS))
+        rows = int(rng.integers(1, 2200))
+        cols = 256 * int(rng.integers(1, 14))
+        entry = ("kq_matvec", "kq_matvec16", "kq_matmul")[case % 3]
+        ntok = int(rng.integers(1, {"kq_matvec": 9, "kq_matvec16": 17, "kq_matmul": 100}[entry]))
+        w = kqgen.weights(fmt, rows, cols, 830, case)
+        x = kqgen.activations(ntok, cols, 831, case)
+        note("random case %d: %s fmt=%d %dx%d ntok=%d" % (case, entry, fmt, rows, cols, ntok))
+        if entry == "kq_matvec":
+            y = gpu_matvec(fmt, w, rows, cols, x)
+        elif entry == "kq_matvec16":
+            y = _gpu_matvec16(fmt, w, rows, cols, x)
+        else:
+            y = _gpu_matmul(fmt, w, rows, cols, x)
+        y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=8)
+        check_tol(y, y_ref, s, "random case %d %s" % (case, entry))
