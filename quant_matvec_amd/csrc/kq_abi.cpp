@@ -46,9 +46,11 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
 // Segment length S: 2 super-blocks, except for matrices whose workgroups
 // get few segments in any launch: any matrix of at most kTinyRows rows, and
 // a Q6_K matrix of at most kSmallRows rows with an odd number of blocks a
-// row, take 1.  A K/V-sized launch then splits into one-block runs, a
-// decode set into runs of similar size, while a large matrix keeps few
-// partial sums.  Depends on (fmt, rows, cols) only, never on ntok.
+// row, take 1; and rows of kLongRowBlocks blocks or more in 32-row tiles
+// take 4.  A K/V-sized launch then splits into one-block runs, a decode set
+// into about one segment per resident wave, while a large matrix keeps few
+// partial sums.  Depends on the tensor's shape and, through the tile
+// height, on ntok; a set member's plan never depends on the other members.
 //
 // Tile rows: 32 for a matrix of more than kTinyRows rows and an even number
 // of blocks a row at one token plane (and at two up to kSmallRows rows),
@@ -56,26 +58,31 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
 // rows share between successive block columns live, more than the L2 holds
 // on a large matrix, and about a third of the lines are read twice; 32-row
 // tiles that take a segment (two columns) a step halve that and stay near
-// one read per line, and give a decode set twice as many, shorter segments.
-// With more token planes the compute per byte grows and 64-row tiles are
-// faster.  Both heights sum the same two-block segments the same way, so a
-// plane's result does not depend on the height.
+// one read per line.  With more token planes the compute per byte grows
+// and 64-row tiles are faster.  Both heights sum the same two-block segments
+// the same way, so where S is 2 in both a plane's result does not depend on
+// the height.
 constexpr int64_t kSmallRows = 16384;
 constexpr int64_t kTinyRows = 1024;
+constexpr int64_t kLongRowBlocks = 20;
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
                  int32_t* tile_rows) {
     const int64_t nb = cols / 256;
     // A matrix of more than kTinyRows rows and an even number of blocks a row
-    // may run in 32-row tiles: always in two-block segments, whatever the
-    // token count, so that every token plane sums the same segments in the
-    // same order in either tile height.
+    // may run in 32-row tiles: at one token plane, and at two up to
+    // kSmallRows rows; with more planes the compute per byte grows and
+    // 64-row tiles run faster.
     const bool pairable = rows > kTinyRows && nb % 2 == 0;
-    const int32_t S = pairable ? 2 : ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
+    *tile_rows = pairable && (ntok == 1 || (ntok == 2 && rows <= kSmallRows)) ? 32 : kTileRows;
+    // In 32-row tiles a row of kLongRowBlocks blocks or more takes four-block
+    // segments (two steps), so a decode set makes about one segment per
+    // resident wave; otherwise a pairable matrix takes two-block segments
+    // in either tile height, so its planes sum alike at any ntok.
+    const int32_t S = (*tile_rows == 32 && nb >= kLongRowBlocks) ? 4
+                      : pairable ? 2
+                      : ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
-    // 32-row tiles at one token plane, and at two up to kSmallRows rows; with
-    // more planes the compute per byte grows and 64-row tiles run faster.
-    *tile_rows = pairable && (ntok == 1 || (ntok == 2 && rows <= kSmallRows)) ? 32 : kTileRows;
 }
 
 static bool ranges_overlap(uintptr_t a0, uintptr_t a1, uintptr_t b0, uintptr_t b1) {

@@ -775,13 +775,15 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
 // with another value at a branch join, where the compiler would copy it and
 // wait for the loads.
 //
-// Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0), carrying the
-// segment index j = tile*nseg + b/S along (it moves on at a segment's last
-// block or a row's end); a column whose segment is >= j1 lies past the end
-// of the run.  S is 1 or 2, so b is a segment's last block when
-// (b & smask) == smask, smask = S - 1.  All of it is 32-bit scalar
-// arithmetic (segment counts fit in int32).
-#define KQ_LAST_OF_SEG(b_) (Col::CPS == 2 || ((b_) & smask) == smask)
+// Positions advance (tile, b) -> (tile, b+1) or (tile+1, 0) (b+2 in 32-row
+// tiles, which take two blocks a step), carrying the segment index
+// j = tile*nseg + b/S along (it moves on at a segment's last step or a
+// row's end); a column whose segment is >= j1 lies past the end of the run.
+// S is 1, 2 or 4 (4 only in 32-row tiles), smask = S - 1: a 64-row step ends
+// its segment when (b & smask) == smask, a 32-row step when b + 2 is a
+// multiple of S.  All of it is 32-bit scalar arithmetic (segment counts fit
+// in int32).
+#define KQ_LAST_OF_SEG(b_) (Col::CPS == 2 ? ((((b_) + 2) & smask) == 0) : (((b_) & smask) == smask))
 #define KQ_ADVANCE(t_, b_, j_)                                      \
     {                                                               \
         if ((b_) + Col::CPS >= nb) { ++(t_); (b_) = 0; ++(j_); }      \

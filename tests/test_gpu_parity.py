@@ -323,6 +323,27 @@ def test_mid_matrix_ntok_columns_bitwise(fmt, ntok):
     check_tol(y, y_ref, s, "mid ntok fmt %d" % fmt)
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_long_row_plans_across_ntok(fmt):
+    """Rows of 26 blocks in 32-row tiles (ntok 1 and 2) take four-block
+    segments, in 64-row tiles (ntok 3 and more) two-block ones: planes
+    match bitwise between calls of the same plan, and every call meets the
+    tolerance."""
+    rows, cols = 4100, 6656
+    w = kqgen.weights(fmt, rows, cols, 627, fmt)
+    x = kqgen.activations(8, cols, 628, fmt)
+    note("long-row plans fmt=%d" % fmt)
+    y1 = np.concatenate([gpu_matvec(fmt, w, rows, cols, x[t:t + 1]) for t in range(2)])
+    y2 = gpu_matvec(fmt, w, rows, cols, x[:2])
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    y3 = gpu_matvec(fmt, w, rows, cols, x[:3])
+    y8 = gpu_matvec(fmt, w, rows, cols, x)
+    assert np.array_equal(y3.view(np.uint32), y8[:3].view(np.uint32))
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=8)
+    check_tol(y2, y_ref[:2], s[:2], "long rows ntok 2")
+    check_tol(y8, y_ref, s, "long rows ntok 8")
+
+
 def test_mixed_tile_set_matches_singles():
     """A set of a 32-row-tile matrix and 64-row-tile ones: every member
     bitwise equal to its own kq_matvec call."""
