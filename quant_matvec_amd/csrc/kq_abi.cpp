@@ -46,10 +46,10 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
 // Segment length S: 2 super-blocks, except for matrices whose workgroups
 // get few segments in any launch: any matrix of at most kTinyRows rows, and
 // a Q6_K matrix of at most kSmallRows rows with an odd number of blocks a
-// row, take 1; and rows of kLongRowBlocks blocks or more in 32-row tiles
-// take 4.  A K/V-sized launch then splits into one-block runs, a decode set
-// into about one segment per resident wave, while a large matrix keeps few
-// partial sums.  Depends on the tensor's shape and, through the tile
+// row, take 1; and long rows in 32-row tiles take 4 unless the matrix has
+// between kSmallRows and 4*kSmallRows rows.  A K/V-sized launch then splits
+// into one-block runs, a decode set into about one segment per resident
+// wave, while a large matrix keeps few partial sums.  Depends on the tensor's shape and, through the tile
 // height, on ntok; a set member's plan never depends on the other members.
 //
 // Tile rows: 32 for a matrix of more than kTinyRows rows and an even number
@@ -75,10 +75,16 @@ void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t*
     const bool pairable = rows > kTinyRows && nb % 2 == 0;
     *tile_rows = pairable && (ntok == 1 || (ntok == 2 && rows <= kSmallRows)) ? 32 : kTileRows;
     // In 32-row tiles a row of kLongRowBlocks blocks or more takes four-block
-    // segments (two steps), so a decode set makes about one segment per
-    // resident wave; otherwise a pairable matrix takes two-block segments
-    // in either tile height, so its planes sum alike at any ntok.
-    const int32_t S = (*tile_rows == 32 && nb >= kLongRowBlocks) ? 4
+    // segments (two steps) on a matrix of at most kSmallRows rows (a decode
+    // set then makes about one segment per resident wave) or of at least
+    // 4*kSmallRows (long runs of whole tiles, fewer partial sums).  In
+    // between (an FFN gate or up projection) four-block runs come out too
+    // coarse over the few segments each wave gets and measure slower.
+    // Otherwise a pairable matrix takes two-block segments in either tile
+    // height, so its planes sum alike at any ntok.
+    const bool long_seg = *tile_rows == 32 && nb >= kLongRowBlocks &&
+                          (rows <= kSmallRows || rows >= 4 * kSmallRows);
+    const int32_t S = long_seg ? 4
                       : pairable ? 2
                       : ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
