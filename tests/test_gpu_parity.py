@@ -344,6 +344,24 @@ def test_long_row_plans_across_ntok(fmt):
     check_tol(y8, y_ref, s, "long rows ntok 8")
 
 
+@pytest.mark.parametrize("fmt", FORMATS)
+def test_long_rows_between_small_and_tall_keep_two_block_segments(fmt):
+    """Rows of 20 blocks on a matrix of 16448 rows (between 16384 and
+    65536 rows, where four-block segments measured slower): two-block
+    segments in 32-row tiles at ntok 1 and in 64-row tiles at ntok 2 and 3,
+    so every plane is bitwise the one-plane call on it."""
+    rows, cols = 16448, 5120
+    w = kqgen.weights(fmt, rows, cols, 629, fmt)
+    x = kqgen.activations(3, cols, 630, fmt)
+    note("long rows mid band fmt=%d" % fmt)
+    y1 = np.concatenate([gpu_matvec(fmt, w, rows, cols, x[t:t + 1]) for t in range(3)])
+    for ntok in (2, 3):
+        y = gpu_matvec(fmt, w, rows, cols, x[:ntok])
+        assert np.array_equal(y1[:ntok].view(np.uint32), y.view(np.uint32)), ntok
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=8)
+    check_tol(y1, y_ref, s, "long rows mid band")
+
+
 def test_mixed_tile_set_matches_singles():
     """A set of a 32-row-tile matrix and 64-row-tile ones: every member
     bitwise equal to its own kq_matvec call."""
