@@ -97,7 +97,8 @@ struct KqPlanSizes {
 int32_t block_bytes(int32_t fmt);
 
 // Segment length S (super-blocks) of one tensor, the segments per tile row
-// and the rows of a tile (64, or 32).  Depends on (fmt, rows, cols) only.
+// and the rows of a tile (64, or 32).  Depends on (fmt, rows, cols) and, through
+// the tile height, on ntok.
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
                  int32_t* tile_rows);
 
