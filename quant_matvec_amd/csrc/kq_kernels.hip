@@ -911,7 +911,11 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     const int j1 = j0 + T.seg_q + (u < T.seg_r ? 1 : 0);
     // 32-row tiles are planned for one and two token planes only
     if constexpr (NTOK <= 2) {
-        constexpr int DP = NTOK == 1 ? 2 : 1;   // 32-row tiles: segments in flight
+        // 32-row tiles keep one block-pair step in flight: with two, a
+        // decode set and the large matrices both ran 1-8% slower (at two
+        // waves a SIMD one step already keeps enough bytes in flight, and
+        // the second register set only adds pressure)
+        constexpr int DP = 1;
         if (T.tile_rows != kTileRows) {
             switch (T.fmt) {
             case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
