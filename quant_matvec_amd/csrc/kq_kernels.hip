@@ -766,8 +766,9 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
 // time.  DEPTH columns are in flight in DEPTH register sets used in turn:
 // the loads of column i+DEPTH go into the set of column i as soon as column
 // i has been written to LDS, so a workgroup's first DEPTH columns are
-// requested at once.  Q4_K and Q5_K use DEPTH 2, Q6_K 1 (36, 44 and 64
-// staging registers a column).
+// requested at once.  In 64-row tiles Q4_K and Q5_K use DEPTH 2, Q6_K 1
+// (36, 44 and 64 staging registers a column); in 32-row tiles every format
+// keeps one block-pair step in flight.
 //
 // The step is written out once per register set (static indices) and every
 // step refills its set unconditionally (a column past the run reads a
