@@ -34,10 +34,17 @@
  *     accumulate in float32 with the per-sub-block scale applied once per
  *     sub-block), so they are not bitwise equal to another kernel's.
  *   - Up to 16 devices; calls on one device that run concurrently on
- *     different streams are safe.  Each (device, stream) pair gets its own
- *     small workspace (partial sums and counters), allocated with hipMalloc
- *     on the first call that needs it -- make that first call outside HIP
- *     graph capture.
+ *     different streams are safe.  kq_matvec and kq_matvec_set split long
+ *     rows between workgroups; the partial sums of the tiles they share go
+ *     to a workspace owned by the library, one per (device, stream).  It is
+ *     allocated (hipMalloc, 64 MB of partial sums) by the first call on that
+ *     stream that needs one -- make that call outside HIP graph capture --
+ *     and is large enough for every plan of a model layer's shapes, since
+ *     the partial sums needed are bounded by the grid and the row length,
+ *     not by the number of rows.  A later plan that needs more gets a larger
+ *     workspace without synchronizing: the old one is kept, never freed
+ *     while work may use it.  No entry point synchronizes or frees.
+ *     kq_release_workspace frees a stream's workspaces.
  */
 #ifndef KQMV_H
 #define KQMV_H
@@ -117,6 +124,15 @@ int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols,
 int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream);
 
 /*
+ * Frees the workspaces kq_matvec / kq_matvec_set hold for `stream` on the
+ * current device (the caller first synchronizes the stream, or destroys it
+ * after this call; no queued work may still use them).  The next call on
+ * that stream allocates afresh.  Returns KQ_OK, or KQ_ERR_HIP if a free
+ * failed.
+ */
+int kq_release_workspace(void* stream);
+
+/*
  * Host-only validation of a set (the checks kq_matvec_set runs before any
  * HIP call).  Makes no HIP call at all.  Returns KQ_OK or the error code
  * kq_matvec_set would return.
@@ -180,7 +196,13 @@ int kq_embed_rows(int32_t fmt, const void* table, int64_t rows, int64_t cols,
 /*
  * Debug/test export: integer decode of `nblocks` consecutive super-blocks
  * starting at w (16-byte aligned), with the same device decoders the matvec
- * kernels use.  Outputs (device pointers, any may be NULL to skip):
+ * kernels use: the f16 headers, the 6-bit scales and mins of the Q4_K/Q5_K
+ * strip (muser-book Ch 6 section 6.2, the get_scale_min rule, Figure 6.3),
+ * the 4- and 5-bit codes (Figures 6.2 and 6.4) and the Q6_K int8 scales and
+ * 6-bit codes with their -32 offset (section 6.4, Figure 6.5).  Enqueued on
+ * `stream`; allocates nothing; all checks on the host (KQ_ERR_FORMAT,
+ * KQ_ERR_ROWS for nblocks <= 0, KQ_ERR_NULL for a null w, KQ_ERR_ALIGN).
+ * Outputs (device pointers, any may be NULL to skip):
  *   codes_out  int32 [nblocks][256]: Q4_K 0..15, Q5_K 0..31,
  *              Q6_K -32..31 (the 6-bit code minus 32)
  *   scales_out int32 [nblocks][16]: Q4_K/Q5_K sc_0..sc_7 then zeros;

@@ -22,7 +22,7 @@ STATUS = {
     -5: "KQ_ERR_NULL", -6: "KQ_ERR_ALIGN", -7: "KQ_ERR_STRIDE", -8: "KQ_ERR_OVERLAP",
     -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE",
 }
-EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set",
+EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set", "kq_release_workspace",
            "kq_matvec16", "kq_matmul", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
            "kq_version")
 
@@ -60,6 +60,8 @@ def load() -> ctypes.CDLL:
         L.kq_matvec_set.restype = ctypes.c_int
         L.kq_validate_set.argtypes = [ctypes.POINTER(kq_tensor), i32, i32]
         L.kq_validate_set.restype = ctypes.c_int
+        L.kq_release_workspace.argtypes = [vp]
+        L.kq_release_workspace.restype = ctypes.c_int
         L.kq_unpack_blocks.argtypes = [i32, vp, i64, vp, vp, vp, vp, vp, vp]
         L.kq_unpack_blocks.restype = ctypes.c_int
         L.kq_dequant.argtypes = [i32, vp, i64, i64, vp, i64, vp]
@@ -175,6 +177,12 @@ def kq_validate_set(tensors, ntok: int = 1, n: int | None = None) -> int:
     arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
     count = len(arr) if n is None else n
     return load().kq_validate_set(arr, count, ntok)
+
+
+def kq_release_workspace(stream=None) -> None:
+    """Free the library's workspaces for `stream` on the current device
+    (synchronize the stream first)."""
+    _check(load().kq_release_workspace(_stream(stream)), "kq_release_workspace")
 
 
 def kq_unpack_blocks(fmt: int, w, nblocks: int, codes=None, scales=None, mins=None, d=None, dmin=None,

@@ -3,15 +3,19 @@
 // and the calls into the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "kq_plan.h"
 
 namespace kq {
 
 int launch_matvec(const KqLaunch& L, hipStream_t stream);
+int launch_capacity(int32_t ntok, int32_t lds_bytes);
+int launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
 int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,
                   int32_t* mins, float* d, float* dmin, hipStream_t stream);
@@ -146,12 +150,12 @@ static int validate_tensors(const kq_tensor* t, int32_t n, int32_t ntok, int32_t
 
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) { return validate_tensors(t, n, ntok, KQ_MAX_NTOK); }
 
-int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPlanSizes* sz) {
+int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L) {
     *L = KqLaunch{};
     L->h.n = n;
     for (int i = 0; i < kMaxSet; ++i) L->h.wg_end[i] = INT32_MAX;
     L->ntok = ntok;
-    int32_t parts = 0, tiles = 0, lds = 0, segs = 0;
+    int32_t lds = 0, segs = 0;
     for (int i = 0; i < n; ++i) {
         const kq_tensor& T = t[i];
         KqDesc& D = L->t[i];
@@ -166,18 +170,20 @@ int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L, KqPla
         D.fmt = T.fmt;
         plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.nseg, &D.seg, &D.tile_rows);
         D.tiles = (int32_t)((T.rows + D.tile_rows - 1) / D.tile_rows);
-        D.part_base = parts;
-        parts += D.tiles * D.nseg;
-        D.tile_base = tiles;
-        tiles += D.tiles;
         segs += D.tiles * D.nseg;
         if (slot_bytes(T.fmt, ntok, D.tile_rows) > lds) lds = slot_bytes(T.fmt, ntok, D.tile_rows);
     }
     L->total_segments = segs;
     L->lds_bytes = lds;
-    sz->partial_floats = (size_t)parts * ntok * kTileRows;
-    sz->counters = (size_t)tiles;
     return KQ_OK;
+}
+
+// Workspace slots of a tensor once its split is set: one per tile while
+// the runs are shorter than a tile, else one per run boundary (the kernel's
+// shared_slot numbers them the same way).
+static int64_t shared_slots(const KqDesc& D) {
+    if (D.wg_count <= 1) return 0;
+    return D.seg_q < D.nseg ? (int64_t)D.tiles : (int64_t)D.wg_count - 1;
 }
 
 // Workgroups of the tensors for a bound C on the bytes of one workgroup's
@@ -197,7 +203,7 @@ static int64_t workgroups_for(const KqLaunch& L, int64_t C, int32_t* per_wg) {
     return P;
 }
 
-void assign_workgroups(KqLaunch* L, int32_t capacity) {
+KqPlanSizes assign_workgroups(KqLaunch* L, int32_t capacity) {
     const int n = L->h.n;
     if (capacity < n) capacity = n;
     // smallest C (bytes) whose split fits in `capacity` workgroups: the
@@ -229,6 +235,8 @@ void assign_workgroups(KqLaunch* L, int32_t capacity) {
         P[i] = (int32_t)(p < segs ? p : segs);
     }
     int32_t base = 0;
+    int64_t slots = 0;
+    KqPlanSizes sz{0, 0};
     for (int i = 0; i < n; ++i) {
         KqDesc& D = L->t[i];
         const int32_t segs = D.tiles * D.nseg;
@@ -238,19 +246,52 @@ void assign_workgroups(KqLaunch* L, int32_t capacity) {
         D.seg_r = segs % P[i];
         base += P[i];
         L->h.wg_end[i] = base;
+        // shared-tile slots: one a tile while runs are shorter than a tile,
+        // else one a run boundary (at most one boundary lies inside a tile)
+        D.part_base = (int32_t)slots;
+        D.tile_base = (int32_t)slots;
+        const int64_t ns = shared_slots(D);
+        slots += ns;
+        sz.partial_floats += (size_t)ns * D.nseg * L->ntok * kTileRows;
     }
     L->grid = base;
+    sz.counters = (size_t)slots;
+    return sz;
+}
+
+void bind_workspace(KqLaunch* L, float* partials, uint32_t* counters) {
+    L->partials = partials;
+    L->counters = counters;
+    size_t off = 0;
+    for (int i = 0; i < L->h.n; ++i) {
+        KqDesc& D = L->t[i];
+        const int64_t ns = shared_slots(D);
+        const bool any = ns > 0 && partials != nullptr;
+        D.partials = any ? partials + off : nullptr;
+        D.counters = any ? counters + D.tile_base : nullptr;
+        off += (size_t)ns * D.nseg * L->ntok * kTileRows;
+    }
 }
 
 // -------------------------------------------------------------- workspaces
-// One per (device, stream): partial sums and the per-tile arrival counters
-// of the column-split fix-up.  Counters are zeroed when allocated and every
-// launch leaves them zero again.
+// One per (device, stream): the shared-tile slots and arrival counters of
+// the fix-up.  Allocated by the first call on that stream that needs one,
+// with room for kWorkspaceFloats slot floats and kWorkspaceCounters counters
+// (the slots are bounded by the grid and the row length, so every plan of
+// the layer shapes at any ntok fits), its counters zeroed by a fill kernel on
+// the stream; every launch leaves the counters it used at zero.  A later
+// plan that needs more gets a new, larger workspace the same way, and the
+// old one stays allocated (kernels already queued on the stream may still
+// use it): no call synchronizes or frees.  kq_release_workspace frees a
+// stream's workspaces once the caller has synchronized it.
+constexpr size_t kWorkspaceFloats = (size_t)16 << 20;     // 64 MB of slot floats
+constexpr size_t kWorkspaceCounters = (size_t)1 << 16;
 struct Workspace {
     float* partials = nullptr;
     size_t partial_cap = 0;
     uint32_t* counters = nullptr;
     size_t counter_cap = 0;
+    std::vector<void*> retired;
 };
 
 static std::mutex g_ws_mutex;
@@ -265,27 +306,62 @@ static int get_workspace(hipStream_t stream, const KqPlanSizes& sz, float** part
     std::lock_guard<std::mutex> lock(g_ws_mutex);
     Workspace& ws = g_ws[std::make_pair(dev, stream)];
     if (ws.partial_cap < sz.partial_floats || ws.counter_cap < sz.counters) {
-        if (ws.partials || ws.counters) {
-            if (hipStreamSynchronize(stream) != hipSuccess) return KQ_ERR_HIP;
-            (void)hipFree(ws.partials);
-            (void)hipFree(ws.counters);
-            ws = Workspace{};
-        }
-        size_t pc = sz.partial_floats < (1u << 20) ? (1u << 20) : sz.partial_floats;
-        size_t cc = sz.counters < (1u << 16) ? (1u << 16) : sz.counters;
-        if (hipMalloc(&ws.partials, pc * sizeof(float)) != hipSuccess) return KQ_ERR_HIP;
-        if (hipMalloc(&ws.counters, cc * sizeof(uint32_t)) != hipSuccess) {
-            (void)hipFree(ws.partials);
-            ws = Workspace{};
+        const size_t pc = std::max({sz.partial_floats, kWorkspaceFloats, 2 * ws.partial_cap});
+        const size_t cc = std::max({sz.counters, kWorkspaceCounters, 2 * ws.counter_cap});
+        float* p = nullptr;
+        uint32_t* c = nullptr;
+        if (hipMalloc(&p, pc * sizeof(float)) != hipSuccess) return KQ_ERR_HIP;
+        if (hipMalloc(&c, cc * sizeof(uint32_t)) != hipSuccess) {
+            (void)hipFree(p);
             return KQ_ERR_HIP;
         }
-        if (hipMemsetAsync(ws.counters, 0, cc * sizeof(uint32_t), stream) != hipSuccess) return KQ_ERR_HIP;
+        if (launch_zero(c, (int64_t)cc, stream) != KQ_OK) {
+            (void)hipFree(p);
+            (void)hipFree(c);
+            return KQ_ERR_HIP;
+        }
+        if (ws.partials) ws.retired.push_back(ws.partials);
+        if (ws.counters) ws.retired.push_back(ws.counters);
+        ws.partials = p;
+        ws.counters = c;
         ws.partial_cap = pc;
         ws.counter_cap = cc;
     }
     *partials = ws.partials;
     *counters = ws.counters;
     return KQ_OK;
+}
+
+static int release_workspace(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KQ_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_ws_mutex);
+    auto it = g_ws.find(std::make_pair(dev, stream));
+    if (it == g_ws.end()) return KQ_OK;
+    int rc = KQ_OK;
+    Workspace& ws = it->second;
+    ws.retired.push_back(ws.partials);
+    ws.retired.push_back(ws.counters);
+    for (void* p : ws.retired)
+        if (p && hipFree(p) != hipSuccess) rc = KQ_ERR_HIP;
+    g_ws.erase(it);
+    return rc;
+}
+
+// Plans and enqueues one launch of the validated set with the stream's
+// workspace.
+static int enqueue_set(const kq_tensor* tensors, int32_t n, int32_t ntok, hipStream_t s) {
+    KqLaunch L;
+    build_launch(tensors, n, ntok, &L);
+    const int cap = launch_capacity(ntok, L.lds_bytes);
+    if (cap <= 0) return KQ_ERR_HIP;
+    const KqPlanSizes sz = assign_workgroups(&L, cap);
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    const int rc = get_workspace(s, sz, &partials, &counters);
+    if (rc != KQ_OK) return rc;
+    bind_workspace(&L, partials, counters);
+    return launch_matvec(L, s);
 }
 
 }  // namespace kq
@@ -308,21 +384,12 @@ int kq_validate_set(const kq_tensor* tensors, int32_t n, int32_t ntok) {
 }
 
 int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream) {
-    int rc = validate_set(tensors, n, ntok);
+    const int rc = validate_set(tensors, n, ntok);
     if (rc != KQ_OK) return rc;
-    KqLaunch L;
-    KqPlanSizes sz;
-    build_launch(tensors, n, ntok, &L, &sz);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    rc = get_workspace(s, sz, &L.partials, &L.counters);
-    if (rc != KQ_OK) return rc;
-    for (int i = 0; i < n; ++i) {
-        KqDesc& D = L.t[i];
-        D.partials = L.partials ? L.partials + (size_t)D.part_base * ntok * kTileRows : nullptr;
-        D.counters = L.counters ? L.counters + D.tile_base : nullptr;
-    }
-    return launch_matvec(L, s);
+    return enqueue_set(tensors, n, ntok, static_cast<hipStream_t>(stream));
 }
+
+int kq_release_workspace(void* stream) { return release_workspace(static_cast<hipStream_t>(stream)); }
 
 int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx,
               float* y, int64_t ldy, int32_t ntok, void* stream) {

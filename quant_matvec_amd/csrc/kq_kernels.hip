@@ -18,13 +18,17 @@
 //     the current column is computed (two columns in flight for Q4_K and
 //     Q5_K, one for Q6_K).
 //   * Codes become binary16 subnormals two per word (kq_decode.h) and feed
-//     v_fma_mix_f32 directly: one instruction per weight for the
-//     multiply-add, plus about 0.6 (Q4_K) to 1.4 (Q6_K) bit operations per
-//     weight to unpack.
-//   * Scales are applied once per sub-block (deferred scaling, muser-book
-//     Ch 13 section 13.4): per sub-block j the lane accumulates
-//     sum(q*x) and adds d*sc_j*that - dmin*m_j*sum(x); sum(x) over each
-//     sub-block is computed once per column by the wave with DPP reductions.
+//     v_fma_mix_f32 directly, with no conversion instruction, plus about 0.6
+//     (Q4_K) to 1.4 (Q6_K) bit operations per weight to unpack.
+//   * Q4_K/Q5_K: every weight is formed with one rounding,
+//     fma(d*sc, q, -dmin*m) (the pages' single-rounding form, muser-book
+//     Ch 13 section 13.4.2), then multiplied into the sub-block's sum: two
+//     instructions per weight at one token plane, 1 + ntok at ntok planes.
+//     Q6_K: the code's -32 offset is taken off the packed codes exactly
+//     (one binary16 add per two weights), the sub-block of 16 sums
+//     (q-32)*x and is scaled once by d*sc.  Either way every rounding is
+//     relative to |W_ij x_j|, so the error is bounded by a multiple of
+//     sum_j |W_ij x_j| even where a block's terms cancel.
 //   * No MFMA: at ntok <= 8 this is a streaming dot product, not a dense
 //     contraction.
 #include <hip/hip_runtime.h>
@@ -47,6 +51,7 @@ typedef __attribute__((address_space(1))) float* gfloat_t;
 __device__ __forceinline__ gfloat_t gfloat(float* p) { return (gfloat_t)(p); }
 
 constexpr float kTwo24 = 16777216.0f;        // undoes the 2^-24 of a subnormal code
+constexpr float kTwo20 = 1048576.0f;         // ... of a high nibble left in place (16 * code * 2^-24)
 
 // ---------------------------------------------------------------- wave sums
 // DPP lane permutations (gfx9 encodings): quad_perm [1,0,3,2], [2,3,0,1],
@@ -100,9 +105,6 @@ __device__ __forceinline__ uint32_t lds_read1(const uint8_t* p) { return *reinte
 // the weights: lane i loads x[4i..4i+3] of the next column into registers,
 // writes them to the wave's LDS x slot next to the weights, and the lanes
 // then read them back with wave-uniform addresses (an LDS broadcast read).
-// On the way the wave forms the sums of x over each sub-block (32 elements
-// for Q4_K/Q5_K, 16 for Q6_K) with DPP: afterwards every lane of group j
-// holds the sum of sub-block j, in a fixed order.
 template <int NTOK>
 struct XStage {
     float4 v[NTOK];
@@ -113,42 +115,16 @@ struct XStage {
             v[t] = __builtin_bit_cast(float4, *(const __attribute__((address_space(1))) u32x4*)(
                                                   gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane)));
     }
-    template <int SUB>
-    __device__ __forceinline__ void commit(uint8_t* xslot, float (&sx)[NTOK]) const {
+    __device__ __forceinline__ void commit(uint8_t* xslot) const {
         const int lane = threadIdx.x;
 #pragma unroll
-        for (int t = 0; t < NTOK; ++t) {
-            reinterpret_cast<float4*>(xslot + 1024 * t)[lane] = v[t];
-            float s = (v[t].x + v[t].y) + (v[t].z + v[t].w);
-            s = s + dpp_xor1(s);
-            s = s + dpp_xor2(s);
-            if (SUB == 32) s = s + dpp_half_mirror(s);
-            sx[t] = s;
-        }
+        for (int t = 0; t < NTOK; ++t) reinterpret_cast<float4*>(xslot + 1024 * t)[lane] = v[t];
     }
 };
 
 __device__ __forceinline__ float4 xread(const uint8_t* xslot, int t, int e) {
     return *reinterpret_cast<const float4*>(xslot + 1024 * t + 4 * e);
 }
-
-// The sum of x over a sub-block, as the lane's block needs it: from the one
-// column of a 64-row tile (Sx1), or from the lane's own column of the two a
-// 32-row tile computes at once (Sx2: even lanes the first, odd the second).
-// `idx` names the lane of the column's DPP reduction that holds the sum.
-template <int NTOK>
-struct Sx1 {
-    float v[NTOK];
-    __device__ __forceinline__ float get(int t, int idx) const { return lane_value(v[t], idx); }
-};
-template <int NTOK>
-struct Sx2 {
-    float v[2][NTOK];
-    __device__ __forceinline__ float get(int t, int idx) const {
-        const float a = lane_value(v[0][t], idx), b = lane_value(v[1][t], idx);
-        return (threadIdx.x & 1) ? b : a;
-    }
-};
 
 // End of one step of a block's multiply-adds: the step's accumulators are
 // complete here and no LDS read of a later step moves above this point.
@@ -175,10 +151,19 @@ struct K45 {
 };
 
 // One group g of a block: sub-blocks 2g (low nibbles) and 2g+1 (high).
-template <int FMT, int NTOK, int G, class SX>
-__device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&qh)[8], const K4Scales& S,
-                                          const uint8_t* xslot, const SX& sx,
-                                          float (&ts_e)[NTOK], float (&ts_o)[NTOK], float (&tm)[NTOK]) {
+// Every weight is formed first, with one rounding, as the pages' fallback
+// form fma(d*sc, q, -dmin*m) (muser-book Ch 13 section 13.4.2; Ch 6 section
+// 6.2): d*sc and dmin*m are exact in float32 (11 x 6 significant bits), and
+// so is (d*sc)*q, so the weight is the exact value correctly rounded, and a
+// weight that is exactly zero stays zero.  The code enters v_fma_mix_f32 as
+// its binary16 subnormal (code * 2^-24, or code * 2^-20 for a high nibble
+// left in place); the 2^24 / 2^20 is folded into d*sc.  Then sum_e W_e x_e
+// per sub-block: every rounding is relative to |W_e x_e|, so the result's
+// error is bounded by a multiple of sum_j |W_ij x_j| (no separate min term
+// that could cancel against the code term).
+template <int FMT, int NTOK, int G>
+__device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&qh)[8], const K4Scales& S, float d,
+                                          float dmin, const uint8_t* xslot, float (&c)[NTOK]) {
     uint32_t qs[8];
     {
         const uint4 a = lds_read4(row + K45<FMT>::QS_OFF + 32 * G);
@@ -186,6 +171,10 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
         qs[0] = a.x; qs[1] = a.y; qs[2] = a.z; qs[3] = a.w;
         qs[4] = b.x; qs[5] = b.y; qs[6] = b.z; qs[7] = b.w;
     }
+    const float a_lo = d * (float)k4_sc(S, 2 * G) * kTwo24;          // exact
+    const float a_hi = d * (float)k4_sc(S, 2 * G + 1) * kTwo20;
+    const float n_lo = -(dmin * (float)k4_m(S, 2 * G));               // exact
+    const float n_hi = -(dmin * (float)k4_m(S, 2 * G + 1));
     float al[NTOK], ah[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) { al[t] = 0.0f; ah[t] = 0.0f; }
@@ -195,62 +184,57 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
         if constexpr (FMT == KQ_Q4_K) p = k4_codes(qs[k]);
         else p = k5_codes<G>(qs[k], qh[k]);
         const int e = 64 * G + 4 * k;
+        const float wl0 = __builtin_fmaf(a_lo, (float)half_lo(p.lo02), n_lo);
+        const float wl1 = __builtin_fmaf(a_lo, (float)half_lo(p.lo13), n_lo);
+        const float wl2 = __builtin_fmaf(a_lo, (float)half_hi(p.lo02), n_lo);
+        const float wl3 = __builtin_fmaf(a_lo, (float)half_hi(p.lo13), n_lo);
+        const float wh0 = __builtin_fmaf(a_hi, (float)half_lo(p.hi02), n_hi);
+        const float wh1 = __builtin_fmaf(a_hi, (float)half_lo(p.hi13), n_hi);
+        const float wh2 = __builtin_fmaf(a_hi, (float)half_hi(p.hi02), n_hi);
+        const float wh3 = __builtin_fmaf(a_hi, (float)half_hi(p.hi13), n_hi);
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
             const float4 xl = xread(xslot, t, e), xh = xread(xslot, t, e + 32);
-            al[t] = __builtin_fmaf((float)half_lo(p.lo02), xl.x, al[t]);
-            al[t] = __builtin_fmaf((float)half_lo(p.lo13), xl.y, al[t]);
-            al[t] = __builtin_fmaf((float)half_hi(p.lo02), xl.z, al[t]);
-            al[t] = __builtin_fmaf((float)half_hi(p.lo13), xl.w, al[t]);
-            ah[t] = __builtin_fmaf((float)half_lo(p.hi02), xh.x, ah[t]);
-            ah[t] = __builtin_fmaf((float)half_lo(p.hi13), xh.y, ah[t]);
-            ah[t] = __builtin_fmaf((float)half_hi(p.hi02), xh.z, ah[t]);
-            ah[t] = __builtin_fmaf((float)half_hi(p.hi13), xh.w, ah[t]);
+            al[t] = __builtin_fmaf(wl0, xl.x, al[t]);
+            al[t] = __builtin_fmaf(wl1, xl.y, al[t]);
+            al[t] = __builtin_fmaf(wl2, xl.z, al[t]);
+            al[t] = __builtin_fmaf(wl3, xl.w, al[t]);
+            ah[t] = __builtin_fmaf(wh0, xh.x, ah[t]);
+            ah[t] = __builtin_fmaf(wh1, xh.y, ah[t]);
+            ah[t] = __builtin_fmaf(wh2, xh.z, ah[t]);
+            ah[t] = __builtin_fmaf(wh3, xh.w, ah[t]);
         }
     }
-    const float sc0 = (float)k4_sc(S, 2 * G), sc1 = (float)k4_sc(S, 2 * G + 1);
-    const float m0 = (float)k4_m(S, 2 * G), m1 = (float)k4_m(S, 2 * G + 1);
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t) {
-        ts_e[t] = __builtin_fmaf(sc0, al[t], ts_e[t]);
-        ts_o[t] = __builtin_fmaf(sc1, ah[t], ts_o[t]);
-        tm[t] = __builtin_fmaf(m0, sx.get(t, 8 * (2 * G)), tm[t]);
-        tm[t] = __builtin_fmaf(m1, sx.get(t, 8 * (2 * G + 1)), tm[t]);
-    }
+    for (int t = 0; t < NTOK; ++t) c[t] = (c[t] + al[t]) + ah[t];
 }
 
 // acc[t] += the contribution of the Q4_K/Q5_K block at `row` (LDS) with x
-// at xslot and x sums sx.
-template <int FMT, int NTOK, class SX>
-__device__ __forceinline__ void block_mac(const uint8_t* row, const uint8_t* xslot, const SX& sx, float (&acc)[NTOK]) {
-    {
-        const uint4 hdr = lds_read4(row);
-        uint32_t qh[8];
-        if constexpr (FMT == KQ_Q5_K) {
-            const uint4 a = lds_read4(row + 16), c = lds_read4(row + 32);
-            qh[0] = a.x; qh[1] = a.y; qh[2] = a.z; qh[3] = a.w;
-            qh[4] = c.x; qh[5] = c.y; qh[6] = c.z; qh[7] = c.w;
-        } else {
+// at xslot, formed from zero (sub-blocks 0..7 summed in order) and then
+// added, so that a block adds the same bits in either tile height.
+template <int FMT, int NTOK>
+__device__ __forceinline__ void block_mac(const uint8_t* row, const uint8_t* xslot, float (&acc)[NTOK]) {
+    const uint4 hdr = lds_read4(row);
+    uint32_t qh[8];
+    if constexpr (FMT == KQ_Q5_K) {
+        const uint4 a = lds_read4(row + 16), c = lds_read4(row + 32);
+        qh[0] = a.x; qh[1] = a.y; qh[2] = a.z; qh[3] = a.w;
+        qh[4] = c.x; qh[5] = c.y; qh[6] = c.z; qh[7] = c.w;
+    } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) qh[i] = 0;
-        }
-        const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
-        const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-        float ts_e[NTOK], ts_o[NTOK], tm[NTOK];
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) { ts_e[t] = 0.0f; ts_o[t] = 0.0f; tm[t] = 0.0f; }
-        k45_group<FMT, NTOK, 0>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        k45_group<FMT, NTOK, 1>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        k45_group<FMT, NTOK, 2>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        k45_group<FMT, NTOK, 3>(row, qh, S, xslot, sx, ts_e, ts_o, tm);
-        const float d24 = d * kTwo24;
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) {
-            const float v = __builtin_fmaf(ts_o[t], 0.0625f, ts_e[t]);   // odd sub-blocks were 16*code
-            acc[t] = __builtin_fmaf(d24, v, acc[t]);
-            acc[t] = __builtin_fmaf(-dmin, tm[t], acc[t]);
-        }
+        for (int i = 0; i < 8; ++i) qh[i] = 0;
     }
+    const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
+    const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
+    float c[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
+    k45_group<FMT, NTOK, 0>(row, qh, S, d, dmin, xslot, c);
+    k45_group<FMT, NTOK, 1>(row, qh, S, d, dmin, xslot, c);
+    k45_group<FMT, NTOK, 2>(row, qh, S, d, dmin, xslot, c);
+    k45_group<FMT, NTOK, 3>(row, qh, S, d, dmin, xslot, c);
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
 }
 
 // Per-lane staging offsets of a 64-row column: 16-byte chunk q = 64*i + lane
@@ -278,7 +262,6 @@ struct K45Offsets {
 template <int FMT, int NTOK>
 struct K45Column {
     static constexpr int TR = kTileRows, CPS = 1;               // tile rows, columns a step
-    typedef Sx1<NTOK> Sx;
     static constexpr int C = K45<FMT>::C;
     static constexpr int BB = K45<FMT>::BB;
     typedef K45Offsets<C> Offsets;
@@ -301,24 +284,19 @@ struct K45Column {
             stg[i] = __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4*)(col + min(o.off[i], max_off)));
         xs.load(T, valid ? b : 0);
     }
-    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+    __device__ __forceinline__ void commit(uint8_t* slot) const {
         const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
-        xs.template commit<32>(slot + K45<FMT>::WSLOT, sx.v);
+        xs.commit(slot + K45<FMT>::WSLOT);
     }
-    // acc[t] += this column's contribution for the lane's row, formed on its
-    // own first (as a 32-row tile forms each block's), so that a segment
-    // sums to the same bits in either tile height
+    // acc[t] += this column's contribution for the lane's row (formed on
+    // its own first, as a 32-row tile forms each block's, so that a segment
+    // sums to the same bits in either tile height)
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const Sx& sx, float (&acc)[NTOK]) {
+                                                   float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
-        float c[NTOK];
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
-        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, sx, c);
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
+        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, acc);
     }
 };
 
@@ -330,7 +308,6 @@ struct K45Column {
 template <int FMT, int NTOK>
 struct K45Pair {
     static constexpr int TR = 32, CPS = 2;                     // tile rows, columns a step
-    typedef Sx2<NTOK> Sx;
     static constexpr int C = K45<FMT>::C, BB = K45<FMT>::BB, C2 = 2 * C;
     static constexpr int N = TR * C2 / 64;                     // loads a lane: C
     static constexpr int WSLOT = TR * 2 * BB;
@@ -363,18 +340,18 @@ struct K45Pair {
         xs0.load(T, valid ? b : 0);
         xs1.load(T, valid ? b + 1 : 1);
     }
-    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+    __device__ __forceinline__ void commit(uint8_t* slot) const {
         const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
-        xs0.template commit<32>(slot + WSLOT, sx.v[0]);
-        xs1.template commit<32>(slot + WSLOT + 1024 * NTOK, sx.v[1]);
+        xs0.commit(slot + WSLOT);
+        xs1.commit(slot + WSLOT + 1024 * NTOK);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const Sx& sx, float (&acc)[NTOK]) {
+                                                   float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
         const int lane = threadIdx.x, k = lane & 1;
-        block_mac<FMT, NTOK>(slot + (lane >> 1) * 2 * BB + k * BB, slot + WSLOT + k * 1024 * NTOK, sx, acc);
+        block_mac<FMT, NTOK>(slot + (lane >> 1) * 2 * BB + k * BB, slot + WSLOT + k * 1024 * NTOK, acc);
     }
 };
 
@@ -398,10 +375,28 @@ __device__ __forceinline__ void q6_read4(const uint8_t* row, int i, uint32_t sh,
     o[3] = __builtin_amdgcn_alignbit(e, a.w, sh);
 }
 
-template <int NTOK, int N, int KH, class SX>
+// The signed Q6_K code q - 32 of both halves of a packed pair: the halves
+// are binary16 subnormals (code or 16*code times 2^-24) and the offset is
+// subtracted as binary16 (neg = -32 or -512 times 2^-24 in both halves).
+// The difference is a multiple of 2^-24 below 2^-14 in magnitude, so the
+// subtraction is exact and yields the signed subnormal (q-32) * 2^-24 (or
+// 16*(q-32) * 2^-24).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t q6_signed(uint32_t p, uint32_t neg) {
+    return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, p) + __builtin_bit_cast(half2_t, neg));
+}
+constexpr uint32_t kQ6NegLo = 0x80208020u;    // -32 * 2^-24 in both halves
+constexpr uint32_t kQ6NegHi = 0x82008200u;    // -512 * 2^-24: the offset of a high nibble left in place
+
+// Sixteen elements l = 16KH..16KH+15 of each quarter c of half N (elements
+// 128N + 32c + l, sub-block 8N + 2c + KH of 16): for each quarter the sum
+// of (q-32)*x over the sub-block, scaled by its int8 scale, goes to tl
+// (quarters 0, 1: codes at 2^-24) or th (quarters 2, 3: at 2^-20).  The
+// code carries its offset (q6_signed), so every rounding is relative to
+// |W_e x_e| and nothing is subtracted after the sum.
+template <int NTOK, int N, int KH>
 __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, const uint32_t (&scw)[4],
-                                               const uint8_t* xslot, const SX& sx,
-                                               float (&tl)[NTOK], float (&th)[NTOK]) {
+                                               const uint8_t* xslot, float (&tl)[NTOK], float (&th)[NTOK]) {
     uint32_t A[4], B[4], H[4];
     q6_read4(row, 16 * N + 4 * KH, sh, A);          // ql bytes 64N + 16KH ..
     q6_read4(row, 16 * N + 8 + 4 * KH, sh, B);      // ql bytes 64N + 32 + 16KH ..
@@ -428,7 +423,12 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
 #pragma unroll
                     for (int t = 0; t < NTOK; ++t) xb[(kk + 1) % 2][c][t] = xread(xslot, t, 128 * N + 32 * c + 4 * (k + 1));
             }
-            const Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+            Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                p.c02[c] = q6_signed(p.c02[c], c < 2 ? kQ6NegLo : kQ6NegHi);
+                p.c13[c] = q6_signed(p.c13[c], c < 2 ? kQ6NegLo : kQ6NegHi);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -447,7 +447,12 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int k = 4 * KH + kk;
-            const Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+            Packed6 p = k6_codes(A[kk], B[kk], H[kk]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                p.c02[c] = q6_signed(p.c02[c], c < 2 ? kQ6NegLo : kQ6NegHi);
+                p.c13[c] = q6_signed(p.c13[c], c < 2 ? kQ6NegLo : kQ6NegHi);
+            }
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 const int e = 128 * N + 32 * c + 4 * k;
@@ -466,23 +471,21 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     for (int c = 0; c < 4; ++c) {
         const int j = 8 * N + 2 * c + KH;                                   // sub-block of 16
         const float scj = (float)(int8_t)(scw[j / 4] >> (8 * (j % 4)));
-        // code - 32: subtract 32*sum(x) in the units of a (2^-24 or 2^-20 per code)
-        const float off = (c < 2) ? -0x1p-19f : -0x1p-15f;
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
-            const float u = __builtin_fmaf(off, sx.get(t, 4 * j), a[c][t]);
-            if (c < 2) tl[t] = __builtin_fmaf(scj, u, tl[t]);
-            else th[t] = __builtin_fmaf(scj, u, th[t]);
+            if (c < 2) tl[t] = __builtin_fmaf(scj, a[c][t], tl[t]);
+            else th[t] = __builtin_fmaf(scj, a[c][t], th[t]);
         }
     }
 }
 
 // acc[t] += the contribution of the Q6_K block whose aligned words start at
-// `row` (LDS), shifted by sh bits, with word 52 given apart; x at xslot, x
-// sums sx.
-template <int NTOK, class SX>
+// `row` (LDS), shifted by sh bits, with word 52 given apart; x at xslot.
+// The block's sum is formed from zero and then added, so that a block adds
+// the same bits in either tile height.
+template <int NTOK>
 __device__ __forceinline__ void q6_block_mac(const uint8_t* row, uint32_t w52, uint32_t sh, const uint8_t* xslot,
-                                             const SX& sx, float (&acc)[NTOK]) {
+                                             float (&acc)[NTOK]) {
     // words 48..51 (scales) and word 52 (scales 14-15 and d, or d alone)
     const uint4 s4 = lds_read4(row + 4 * 48);
     uint32_t scw[4];
@@ -494,14 +497,13 @@ __device__ __forceinline__ void q6_block_mac(const uint8_t* row, uint32_t w52, u
     float tl[NTOK], th[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
-    q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, sx, tl, th);
-    q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, sx, tl, th);
-    q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, sx, tl, th);
-    q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, sx, tl, th);
+    q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, tl, th);
+    q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, tl, th);
+    q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, tl, th);
+    q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, tl, th);
     const float d24 = d * kTwo24;
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t)
-        acc[t] = __builtin_fmaf(d24, __builtin_fmaf(th[t], 0.0625f, tl[t]), acc[t]);
+    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + d24 * __builtin_fmaf(th[t], 0.0625f, tl[t]);
 }
 
 // Per-lane staging offsets of a 64-row Q6_K column.  Chunk q = 64*i + lane
@@ -543,8 +545,6 @@ struct Q6Offsets {
 template <int NTOK, bool ALT>
 struct Q6Column {
     static constexpr int TR = kTileRows, CPS = 1;               // tile rows, columns a step
-    typedef Sx1<NTOK> Sx;
-    static constexpr int SUB = 16;
     static constexpr int WSLOT = kTileRows * kQ6LdsRow + 4 * kTileRows;
     typedef Q6Offsets<ALT> Offsets;
     uint4 stg[kQ6Chunks];
@@ -582,27 +582,22 @@ struct Q6Column {
         tailv = *(const __attribute__((address_space(1))) uint16_t*)(gbytes(T.w) + (tail ? last + 208 : 0));
         xs.load(T, valid ? b : 0);
     }
-    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+    __device__ __forceinline__ void commit(uint8_t* slot) const {
         const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < kQ6Chunks; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         reinterpret_cast<uint32_t*>(slot + kTileRows * kQ6LdsRow)[lane] = lane == tail_row ? tailv : w52;
-        xs.template commit<16>(slot + WSLOT, sx.v);
+        xs.commit(slot + WSLOT);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const Sx& sx, float (&acc)[NTOK]) {
+                                                   float (&acc)[NTOK]) {
         const int lane = threadIdx.x;
         // the block starts 2 bytes into its first staged word when its index
         // in the tensor, (r0+lane)*nb + b, is odd
         const uint32_t sh = !ALT ? 16u * (uint32_t)(b & 1)
                                  : 16u * (uint32_t)(((int64_t)(tile * kTileRows + lane) * T.nb + b) & 1);
-        float c[NTOK];                  // formed on its own, as in K45Column
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
         q6_block_mac<NTOK>(slot + lane * kQ6LdsRow, lds_read1(slot + kTileRows * kQ6LdsRow + 4 * lane), sh,
-                           slot + WSLOT, sx, c);
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
+                           slot + WSLOT, acc);
     }
 };
 
@@ -617,7 +612,6 @@ struct Q6Column {
 template <int NTOK>
 struct Q6Pair {
     static constexpr int TR = 32, CPS = 2;                     // tile rows, columns a step
-    typedef Sx2<NTOK> Sx;
     static constexpr int CH = 26;                              // chunks of a row's pair
     static constexpr int ROWB = 16 * CH;                       // 416: odd multiple of 16
     static constexpr int N = TR * CH / 64;                     // loads a lane: 13
@@ -655,21 +649,21 @@ struct Q6Pair {
         xs0.load(T, valid ? b : 0);
         xs1.load(T, valid ? b + 1 : 1);
     }
-    __device__ __forceinline__ void commit(uint8_t* slot, Sx& sx) const {
+    __device__ __forceinline__ void commit(uint8_t* slot) const {
         const int lane = threadIdx.x;
 #pragma unroll
         for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         reinterpret_cast<uint32_t*>(slot + TR * ROWB)[lane & 31] = w104;     // lanes 32..63 repeat 0..31
-        xs0.template commit<16>(slot + WSLOT, sx.v[0]);
-        xs1.template commit<16>(slot + WSLOT + 1024 * NTOK, sx.v[1]);
+        xs0.commit(slot + WSLOT);
+        xs1.commit(slot + WSLOT + 1024 * NTOK);
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
-                                                   const Sx& sx, float (&acc)[NTOK]) {
+                                                   float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
         const int lane = threadIdx.x, k = lane & 1, r = lane >> 1;
         const uint8_t* rowp = slot + r * ROWB + k * 208;
         const uint32_t w52 = k ? lds_read1(slot + TR * ROWB + 4 * r) : lds_read1(rowp + 208);
-        q6_block_mac<NTOK>(rowp, w52, k ? 16u : 0u, slot + WSLOT + k * 1024 * NTOK, sx, acc);
+        q6_block_mac<NTOK>(rowp, w52, k ? 16u : 0u, slot + WSLOT + k * 1024 * NTOK, acc);
     }
 };
 
@@ -687,15 +681,30 @@ __device__ __forceinline__ void write_rows(const KqDesc& T, int tile, const floa
     }
 }
 
+// The workspace slot of a tile that several workgroups share.  Run v of
+// the tensor starts at segment B_v = v*q + min(v, r) (q = seg_q, r = seg_r),
+// and a tile is shared iff some B_v (1 <= v < P) falls strictly inside it.
+// Runs shorter than a tile (q < nseg): the slot is the tile (the runs cover
+// fewer segments than P * nseg, so there are fewer tiles than P).  Runs of
+// a tile or more: a tile holds at most one boundary, and the slot is v - 1
+// for the first boundary v after the tile's first segment.  Either way the
+// workspace holds at most min(tiles, P - 1) slots of nseg segment sums,
+// bounded by the grid and the row length, not by the number of rows.
+__device__ __forceinline__ int shared_slot(const KqDesc& T, int tile) {
+    const int q = T.seg_q, r = T.seg_r;
+    if (q < T.nseg) return tile;
+    const int t0 = tile * T.nseg;                   // segments before the tile
+    return t0 < r * (q + 1) ? t0 / (q + 1) : (t0 - r) / q;
+}
+
 // Segment sum of a shared tile -> its workspace slot.  Partials and counters
 // are only ever touched with device-scope atomic loads and stores, which the
 // hardware keeps coherent across the XCDs' L2 caches (they carry the
 // device-coherence bit), so no L2-wide writeback/invalidate is needed.
 template <int NTOK>
-__device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L, int tile, int seg,
-                                              const float (&v)[NTOK]) {
+__device__ __forceinline__ void store_partial(const KqDesc& T, int slot, int seg, const float (&v)[NTOK]) {
     const int lane = threadIdx.x;
-    gfloat_t dst = gfloat(T.partials) + ((size_t)tile * T.nseg + seg) * (NTOK * kTileRows);
+    gfloat_t dst = gfloat(T.partials) + ((size_t)slot * T.nseg + seg) * (NTOK * kTileRows);
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
         __hip_atomic_store(dst + t * kTileRows + lane, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -707,9 +716,9 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, const KqLaunch& L
 // returned; it adds all segment sums of the tile in order and resets the
 // counter for the next launch.
 template <int NTOK, int TR>
-__device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int tile, int count) {
+__device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int count) {
     const int lane = threadIdx.x;
-    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + tile);
+    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
     uint32_t old = 0;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
@@ -718,7 +727,7 @@ __device__ __forceinline__ void arrive(const KqDesc& T, const KqLaunch& L, int t
     old = __builtin_amdgcn_readfirstlane(old);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     if (old + (uint32_t)count != (uint32_t)T.nseg) return;
-    gfloat_t src = gfloat(T.partials) + (size_t)tile * T.nseg * (NTOK * kTileRows) + lane;
+    gfloat_t src = gfloat(T.partials) + (size_t)slot * T.nseg * (NTOK * kTileRows) + lane;
     float sum[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
@@ -793,8 +802,7 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
 #define KQ_STEP(k_)                                                                            \
     {                                                                                          \
         __syncthreads();                                /* earlier reads of the slot done */   \
-        typename Col::Sx sx;                                                                   \
-        c[k_].commit(slot, sx);                                                                \
+        c[k_].commit(slot);                                                                    \
         late_priority(t_start);                                                                \
         {                                                                                      \
             const bool valid = ij < j1;                                                        \
@@ -808,7 +816,7 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
         const int nj = seg_end ? j + 1 : j;                                                    \
         const bool has_next = nj < j1;                                                         \
         __syncthreads();                                /* slot written */                     \
-        Col::compute(T, slot, tile, b, sx, acc);                                               \
+        Col::compute(T, slot, tile, b, acc);                                                   \
         if (seg_end) {                                                                         \
             if constexpr (Col::TR != kTileRows) {       /* the pair's two blocks */            \
                 _Pragma("unroll") for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + dpp_xor1(acc[t]); \
@@ -816,7 +824,7 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
             if (owned) {                                                                       \
                 _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = tsum[t] + acc[t];   \
             } else {                                                                           \
-                store_partial<NTOK>(T, L, tile, seg, acc);                                     \
+                store_partial<NTOK>(T, wslot, seg, acc);                                       \
                 ++pending;                                                                     \
             }                                                                                  \
             _Pragma("unroll") for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;                    \
@@ -825,21 +833,24 @@ __device__ __forceinline__ void late_priority(uint64_t t_start) {
                     write_rows<NTOK, Col::TR>(T, tile, tsum);                                  \
                     _Pragma("unroll") for (int t = 0; t < NTOK; ++t) tsum[t] = 0.0f;           \
                 } else {                                                                       \
-                    arrive<NTOK, Col::TR>(T, L, tile, pending);                                \
+                    arrive<NTOK, Col::TR>(T, tile, wslot, pending);                            \
                     pending = 0;                                                               \
                 }                                                                              \
             }                                                                                  \
             seg = row_end ? 0 : seg + 1;                                                       \
         }                                                                                      \
         if (!has_next) break;                                                                  \
-        if (row_end) owned = nj >= j0 && nj + nseg <= j1;                                      \
+        if (row_end) {                                                                         \
+            owned = nj + nseg <= j1;                                                           \
+            if (!owned) wslot = shared_slot(T, ntile);                                         \
+        }                                                                                      \
         tile = ntile;                                                                          \
         b = nbb;                                                                               \
         j = nj;                                                                                \
     }
 
 template <class Col, int NTOK, int DEPTH>
-__device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L, int j0, int j1, uint8_t* slot) {
+__device__ __forceinline__ void run_segments(const KqDesc& T, int j0, int j1, uint8_t* slot) {
     const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
     static_assert(DEPTH >= 1 && DEPTH <= 3, "1..3 register sets");
     const int nseg = T.nseg, nb = T.nb, smask = T.seg - 1;
@@ -854,6 +865,7 @@ __device__ __forceinline__ void run_segments(const KqDesc& T, const KqLaunch& L,
     for (int t = 0; t < NTOK; ++t) { acc[t] = 0.0f; tsum[t] = 0.0f; }
     int pending = 0;
     bool owned = seg == 0 && j0 + nseg <= j1;
+    int wslot = owned ? 0 : shared_slot(T, tile);     // workspace slot of a shared tile
     Col c[DEPTH];
     int itile = tile, ib = b, ij = j;     // the next column to request
 #pragma unroll
@@ -919,19 +931,19 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
         constexpr int DP = 1;
         if (T.tile_rows != kTileRows) {
             switch (T.fmt) {
-            case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
-            case KQ_Q5_K: run_segments<K45Pair<KQ_Q5_K, NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
-            default: run_segments<Q6Pair<NTOK>, NTOK, DP>(T, L, j0, j1, slot); break;
+            case KQ_Q4_K: run_segments<K45Pair<KQ_Q4_K, NTOK>, NTOK, DP>(T, j0, j1, slot); break;
+            case KQ_Q5_K: run_segments<K45Pair<KQ_Q5_K, NTOK>, NTOK, DP>(T, j0, j1, slot); break;
+            default: run_segments<Q6Pair<NTOK>, NTOK, DP>(T, j0, j1, slot); break;
             }
             return;
         }
     }
     switch (T.fmt) {
-    case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, L, j0, j1, slot); break;
-    case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, L, j0, j1, slot); break;
+    case KQ_Q4_K: run_segments<K45Column<KQ_Q4_K, NTOK>, NTOK, kDepthQ4>(T, j0, j1, slot); break;
+    case KQ_Q5_K: run_segments<K45Column<KQ_Q5_K, NTOK>, NTOK, kDepthQ5>(T, j0, j1, slot); break;
     default:
-        if (T.nb & 1) run_segments<Q6Column<NTOK, true>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot);
-        else run_segments<Q6Column<NTOK, false>, NTOK, kDepthQ6<NTOK>>(T, L, j0, j1, slot);
+        if (T.nb & 1) run_segments<Q6Column<NTOK, true>, NTOK, kDepthQ6<NTOK>>(T, j0, j1, slot);
+        else run_segments<Q6Column<NTOK, false>, NTOK, kDepthQ6<NTOK>>(T, j0, j1, slot);
         break;
     }
 }
@@ -990,12 +1002,14 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
 // - lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], so lane
 //   (r, g) = (l % 16, l / 16) brings row r's elements 64g..64g+63 of the block
 //   and token r's x over the same elements, one element a product;
-// - A is sc*q of the element (an integer below 2^13, exact in float32), B
-//   is x as given (float32), so the products are the pages' code times x;
+// - A is the element's weight and B is x as given (float32).  For Q4_K and
+//   Q5_K the weight is fma(d*sc, q, -dmin*m), the exact value rounded once
+//   (d*sc, dmin*m and (d*sc)*q are exact in float32), so the products sum
+//   W*x directly and nothing is subtracted afterwards.  For Q6_K A is
+//   sc*(q-32), an integer below 2^12 in magnitude (exact), and C is scaled
+//   by the rows' d afterwards: either way every rounding is relative to
+//   |W_e x_e|;
 // - lane l ends with C[4(l/16) + i][l % 16], i < 4: four rows of one token.
-// Then C is scaled by the rows' d, and the min term dmin * sum_s m_s * sum(x
-// over sub-block s) is formed by two more products (A = m of the lane's two
-// sub-blocks, B = the token's x sums over them).  Everything is float32.
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // One block's operands for a lane: the raw bytes of its row's group g and
@@ -1014,8 +1028,16 @@ struct Mm16Raw {
                                          int g) {
         if constexpr (FMT == KQ_Q6_K) {
             // n = g/2: ql[64n..64n+63], qh[32n..32n+31], scales 4g..4g+3, read as
-            // aligned words from the block's 4-byte-aligned base (the extra word
-            // of each run stays inside the block)
+            // aligned words from the block's 4-byte-aligned base a.  A block
+            // 2 bytes into a word (sh = 16) spans words 0..52 of a, all its
+            // own but the first and last two bytes; a 4-byte-aligned one
+            // (sh = 0) spans words 0..51 and bytes 0-1 of word 52, which end
+            // it.  The words read are a[16n .. 16n+16] (ql, highest 32),
+            // a[32+8n .. 40+8n] (qh, highest 48) and a[48+g], a[48+g+1]
+            // (scales): the last is read only for sh = 16 (word 52 at g = 3,
+            // inside the block); with sh = 0 the alignment ignores it, and
+            // a[48+g] is read again, so nothing past byte 209 of the block
+            // is read.  d of the output rows: the two bytes at 208.
             const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
             sh = (reinterpret_cast<uintptr_t>(blk) & 2) ? 16u : 0u;
             const int n = g >> 1;
@@ -1024,11 +1046,15 @@ struct Mm16Raw {
 #pragma unroll
             for (int i = 0; i < 9; ++i) qh[i] = a[32 + 8 * n + i];
             scw[0] = a[48 + g];
-            scw[1] = a[49 + g];
+            scw[1] = a[48 + g + (sh >> 4)];
 #pragma unroll
             for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint16_t*>(oblk[i] + 208);
         } else {
+            // the lane's own block only: its weights are formed whole in A
             constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;
+            (void)oblk;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ohdr[i] = 0;
             hdr = *reinterpret_cast<const uint4*>(blk);
             q0 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g);
             q1 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g + 16);
@@ -1036,8 +1062,6 @@ struct Mm16Raw {
                 h0 = *reinterpret_cast<const uint4*>(blk + 16);
                 h1 = *reinterpret_cast<const uint4*>(blk + 32);
             }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint32_t*>(oblk[i]);
         }
         if constexpr (WITHX) {
             const float4* xp = reinterpret_cast<const float4*>(xb);
@@ -1046,15 +1070,14 @@ struct Mm16Raw {
         }
     }
 
-    // sc*q of elements 64g..64g+63 in element order, and (Q4_K/Q5_K) the
-    // mins of the two sub-blocks
-    __device__ __forceinline__ void codes(int g, float (&a)[64], float& m_lo, float& m_hi) const {
+    // The A operands of elements 64g..64g+63 in element order: Q6_K
+    // sc*(q-32), Q4_K/Q5_K the weight d*sc*q - dmin*m rounded once.
+    __device__ __forceinline__ void codes(int g, float (&a)[64]) const {
         if constexpr (FMT == KQ_Q6_K) {
             // element 64g + j is n = g/2, k = 2(g%2) + j/32, l = j%32 of the layout:
             // byte j of the ql run (nibble g%2), bits 2k..2k+1 of qh[32n + j%32],
             // sub-block of 16: 4g + j/16
             const int nib = 4 * (g & 1);
-            m_lo = m_hi = 0.0f;
             uint32_t L[16], H[8];
 #pragma unroll
             for (int i = 0; i < 16; ++i) L[i] = __builtin_amdgcn_alignbit(ql[i + 1], ql[i], sh);
@@ -1070,9 +1093,9 @@ struct Mm16Raw {
             }
         } else {
             const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-            const float sl = (float)k4_sc(S, 2 * g), shs = (float)k4_sc(S, 2 * g + 1);
-            m_lo = (float)k4_m(S, 2 * g);
-            m_hi = (float)k4_m(S, 2 * g + 1);
+            const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
+            const float sl = d * (float)k4_sc(S, 2 * g), shs = d * (float)k4_sc(S, 2 * g + 1);   // exact
+            const float nl = -(dmin * (float)k4_m(S, 2 * g)), nh = -(dmin * (float)k4_m(S, 2 * g + 1));
             const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
             const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
 #pragma unroll
@@ -1085,8 +1108,8 @@ struct Mm16Raw {
                         lo |= ((h[i] >> (8 * c + 2 * g)) & 1u) << 4;
                         hi |= ((h[i] >> (8 * c + 2 * g + 1)) & 1u) << 4;
                     }
-                    a[4 * i + c] = sl * (float)lo;
-                    a[32 + 4 * i + c] = shs * (float)hi;
+                    a[4 * i + c] = __builtin_fmaf(sl, (float)lo, nl);
+                    a[32 + 4 * i + c] = __builtin_fmaf(shs, (float)hi, nh);
                 }
             }
         }
@@ -1094,10 +1117,11 @@ struct Mm16Raw {
 };
 
 // acc[i] += one block's contribution to the lane's four outputs, from the
-// block's sc*q values a, mins and row headers, and one 16-token tile of x
+// block's A operands a (and, for Q6_K, the output rows' d) and one 16-token
+// tile of x
 template <int FMT>
-__device__ __forceinline__ void mm16_products(const float (&a)[64], float m_lo, float m_hi,
-                                              const uint32_t (&ohdr)[4], const float4 (&x4)[16], float (&acc)[4]) {
+__device__ __forceinline__ void mm16_products(const float (&a)[64], const uint32_t (&ohdr)[4], const float4 (&x4)[16],
+                                              float (&acc)[4]) {
     // a lane past ntok carries the last plane's x: its product column is
     // never written, and a column of C depends only on its own B column
     float xv[64];
@@ -1112,30 +1136,20 @@ __device__ __forceinline__ void mm16_products(const float (&a)[64], float m_lo, 
 #pragma unroll
     for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
     if constexpr (FMT == KQ_Q6_K) {
-        (void)m_lo; (void)m_hi;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i]), C[i], acc[i]);
     } else {
-        float slo = 0.0f, shi = 0.0f;
+        (void)ohdr;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) { slo += xv[j]; shi += xv[32 + j]; }
-        f32x4 C2 = {0.0f, 0.0f, 0.0f, 0.0f};
-        C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_lo, slo, C2, 0, 0, 0);
-        C2 = __builtin_amdgcn_mfma_f32_16x16x4f32(m_hi, shi, C2, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i] & 0xFFFFu), C[i], acc[i]);
-            acc[i] = __builtin_fmaf(-f16_to_f32(ohdr[i] >> 16), C2[i], acc[i]);
-        }
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + C[i];
     }
 }
 
 template <int FMT>
 __device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
     float a[64];
-    float m_lo, m_hi;
-    r.codes(g, a, m_lo, m_hi);
-    mm16_products<FMT>(a, m_lo, m_hi, r.ohdr, r.xv, acc);
+    r.codes(g, a);
+    mm16_products<FMT>(a, r.ohdr, r.xv, acc);
 }
 
 // A workgroup of `waves` (1, 2 or 4) waves takes one 16-row tile: wave s
@@ -1263,8 +1277,7 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
         for (int i = 0; i < kXR; ++i)
             *reinterpret_cast<u32x4*>(xs + ((tid >> 6) + 4 * i) * kMmXRow + 16 * (tid & 63)) = xr[i];
         float a[64];
-        float m_lo, m_hi;
-        r.codes(g, a, m_lo, m_hi);
+        r.codes(g, a);
         uint32_t oh[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) oh[i] = r.ohdr[i];
@@ -1277,7 +1290,7 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
             const uint8_t* src = xs + (16 * t + r16) * kMmXRow + 256 * g;
 #pragma unroll
             for (int i = 0; i < 16; ++i) x4[i] = *reinterpret_cast<const float4*>(src + 16 * i);
-            mm16_products<FMT>(a, m_lo, m_hi, oh, x4, acc[t]);
+            mm16_products<FMT>(a, oh, x4, acc[t]);
         }
     }
 #undef KQ_MM_LOAD
@@ -1583,26 +1596,55 @@ static int compute_units() {
 }
 
 template <int NTOK>
-static int launch_t(KqLaunch L, hipStream_t stream) {
+static int capacity_t(int lds_bytes) {
     const int cus = compute_units();
     if (cus <= 0) return KQ_ERR_HIP;
-    const int per_cu = min(resident_per_cu<NTOK>(L.lds_bytes), kMaxWavesPerCU);
-    assign_workgroups(&L, per_cu * cus);
-    hipLaunchKernelGGL(kq_matvec_kernel<NTOK>, dim3(L.grid), dim3(64), (size_t)L.lds_bytes, stream, L);
+    return min(resident_per_cu<NTOK>(lds_bytes), kMaxWavesPerCU) * cus;
+}
+
+// One round of resident one-wave workgroups of kq_matvec_kernel<ntok> with
+// this LDS size on the current device (at most two waves a SIMD).
+int launch_capacity(int32_t ntok, int32_t lds_bytes) {
+    switch (ntok) {
+    case 1: return capacity_t<1>(lds_bytes);
+    case 2: return capacity_t<2>(lds_bytes);
+    case 3: return capacity_t<3>(lds_bytes);
+    case 4: return capacity_t<4>(lds_bytes);
+    case 5: return capacity_t<5>(lds_bytes);
+    case 6: return capacity_t<6>(lds_bytes);
+    case 7: return capacity_t<7>(lds_bytes);
+    default: return capacity_t<8>(lds_bytes);
+    }
+}
+
+// The launch L, fully planned (workgroups assigned, workspace set).
+int launch_matvec(const KqLaunch& L, hipStream_t stream) {
+    const dim3 grid((unsigned)L.grid), block(64);
+    const size_t lds = (size_t)L.lds_bytes;
+    switch (L.ntok) {
+    case 1: hipLaunchKernelGGL(kq_matvec_kernel<1>, grid, block, lds, stream, L); break;
+    case 2: hipLaunchKernelGGL(kq_matvec_kernel<2>, grid, block, lds, stream, L); break;
+    case 3: hipLaunchKernelGGL(kq_matvec_kernel<3>, grid, block, lds, stream, L); break;
+    case 4: hipLaunchKernelGGL(kq_matvec_kernel<4>, grid, block, lds, stream, L); break;
+    case 5: hipLaunchKernelGGL(kq_matvec_kernel<5>, grid, block, lds, stream, L); break;
+    case 6: hipLaunchKernelGGL(kq_matvec_kernel<6>, grid, block, lds, stream, L); break;
+    case 7: hipLaunchKernelGGL(kq_matvec_kernel<7>, grid, block, lds, stream, L); break;
+    default: hipLaunchKernelGGL(kq_matvec_kernel<8>, grid, block, lds, stream, L); break;
+    }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
-int launch_matvec(const KqLaunch& L, hipStream_t stream) {
-    switch (L.ntok) {
-    case 1: return launch_t<1>(L, stream);
-    case 2: return launch_t<2>(L, stream);
-    case 3: return launch_t<3>(L, stream);
-    case 4: return launch_t<4>(L, stream);
-    case 5: return launch_t<5>(L, stream);
-    case 6: return launch_t<6>(L, stream);
-    case 7: return launch_t<7>(L, stream);
-    default: return launch_t<8>(L, stream);
-    }
+// Zeroes n words at p on `stream` (a fill kernel, not a memset node, so
+// the call can sit in a captured graph).
+__global__ void kq_zero_kernel(uint32_t* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+int launch_zero(uint32_t* p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return KQ_OK;
+    hipLaunchKernelGGL(kq_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,

@@ -19,9 +19,12 @@
 // boundaries.  The P_i are chosen so that the largest run, in weight bytes,
 // is as small as the round of resident waves allows.  A tile whose segments
 // all belong to one workgroup is summed in registers and written directly;
-// a tile shared by workgroups has its segment sums written to a per-stream
-// workspace, and the last contributor (an arrival counter per tile) adds
-// them in order.
+// a tile shared by workgroups has its segment sums written to a workspace
+// slot, and the last contributor (an arrival counter per slot) adds them in
+// order.  A shared tile holds a run boundary, and its slot is numbered by
+// the first boundary inside it, so a tensor of P workgroups needs at most
+// P - 1 slots of nseg * ntok * 64 floats: the workspace is bounded by the
+// grid and the row length, not by the number of rows.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -56,14 +59,14 @@ struct KqDesc {
     int32_t tiles;      // ceil(rows / 64)
     int32_t nseg;       // segments per tile row
     int32_t seg;        // S: super-blocks per segment (the last one of a row may be shorter)
-    int32_t part_base;  // first partial-sum slot (one per segment) in the workspace
-    int32_t tile_base;  // first counter in the workspace
+    int32_t part_base;  // first shared-tile slot of this tensor in the workspace
+    int32_t tile_base;  // first counter (one per shared-tile slot) in the workspace
     int32_t wg_base;    // first workgroup of this tensor
     int32_t wg_count;   // P_i: workgroups of this tensor
     int32_t seg_q;      // workgroup u of the tensor streams segments [u*seg_q + min(u, seg_r), ...),
     int32_t seg_r;      //   seg_q + (u < seg_r) of them
-    float* partials;    // this tensor's partial sums in the workspace: [segments][ntok][64]
-    uint32_t* counters; // this tensor's arrival counters: one per tile, zero between calls
+    float* partials;    // this tensor's shared-tile slots in the workspace: [P-1][nseg][ntok][64]
+    uint32_t* counters; // this tensor's arrival counters: one per slot, zero between calls
     int32_t tile_rows;  // 64, or 32 for a large matrix (two lanes a row, a segment a step)
     int32_t reserved0;
     int64_t reserved1;
@@ -81,8 +84,8 @@ static_assert(sizeof(KqHead) == 96, "head is three 32-byte groups");
 struct KqLaunch {
     KqHead h;
     KqDesc t[kMaxSet];
-    float* partials;      // workspace base: [segments][ntok][64]
-    uint32_t* counters;   // workspace base: one per tile
+    float* partials;      // workspace base: shared-tile slots of every tensor
+    uint32_t* counters;   // workspace base: one counter per slot
     int32_t ntok;
     int32_t grid;         // workgroups
     int32_t lds_bytes;
@@ -108,13 +111,18 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows);
 // Checks (no HIP calls) of a set; KQ_OK or a KQ_ERR_* code.
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok);
 
-// Fills `out` (workspace pointers and the workgroup split left unset) and
-// the workspace sizes.  Assumes validate_set passed.
-int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out, KqPlanSizes* sizes);
+// Fills `out` (workspace pointers and the workgroup split left unset).
+// Assumes validate_set passed.
+int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out);
 
 // Splits the launch's workgroups between its tensors for at most
-// `capacity` workgroups: sets wg_base, wg_count, seg_q, seg_r of every
-// tensor, the head's wg_end and the grid.
-void assign_workgroups(KqLaunch* L, int32_t capacity);
+// `capacity` workgroups: sets wg_base, wg_count, seg_q, seg_r, part_base
+// and tile_base of every tensor, the head's wg_end and the grid, and
+// returns the workspace the split needs (shared-tile slots and counters).
+KqPlanSizes assign_workgroups(KqLaunch* L, int32_t capacity);
+
+// Points every tensor's partials and counters into a workspace of the size
+// assign_workgroups returned (null pointers for a tensor that needs none).
+void bind_workspace(KqLaunch* L, float* partials, uint32_t* counters);
 
 }  // namespace kq

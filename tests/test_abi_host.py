@@ -191,3 +191,42 @@ def test_matmul_admission(lib):
     assert lib.kq_matmul(12, W, 256, 6656, X, 6656, Y, 255, 512, None) == -7
     # 512 planes of y reaching into x
     assert lib.kq_matmul(12, W, 256, 6656, X, 6656, X - 512 * 256 * 4 + 1024, 256, 512, None) == -8
+
+
+# ---- the workspace slots of shared tiles.  The rule (restated here from
+# the plan's description) numbers a shared tile by itself while runs are
+# shorter than a tile, else by the first run boundary inside it; every
+# contributor of a tile must find the same slot, distinct tiles distinct
+# slots, and every slot must lie below the count the host allocates.
+
+def _runs(segs, P):
+    q, r = divmod(segs, P)
+    starts = [u * q + min(u, r) for u in range(P)] + [segs]
+    return q, r, starts
+
+
+def _slot(tile, nseg, q, r):
+    if q < nseg:
+        return tile
+    t0 = tile * nseg
+    return t0 // (q + 1) if t0 < r * (q + 1) else (t0 - r) // q
+
+
+@pytest.mark.parametrize("tiles,nseg,P", [(272, 7, 2000), (6314, 7, 2048), (4, 26, 104), (3157, 13, 2048),
+                                          (104, 39, 2048), (1, 26, 13), (5, 3, 7), (7, 5, 6), (100, 1, 37),
+                                          (64, 13, 832), (13, 7, 45), (9, 11, 10)])
+def test_shared_tile_slots_unique_and_bounded(tiles, nseg, P):
+    segs = tiles * nseg
+    P = min(P, segs)
+    q, r, starts = _runs(segs, P)
+    nslots = 0 if P <= 1 else (tiles if q < nseg else P - 1)
+    owner = {}
+    for u in range(P):
+        j0, j1 = starts[u], starts[u + 1]
+        for tile in range(j0 // nseg, (j1 - 1) // nseg + 1):
+            t0, t1 = tile * nseg, tile * nseg + nseg
+            if j0 <= t0 and t1 <= j1:
+                continue                              # owned: summed in registers
+            s = _slot(tile, nseg, q, r)
+            assert 0 <= s < nslots, (u, tile, s, nslots)
+            assert owner.setdefault(s, tile) == tile, (s, owner[s], tile)

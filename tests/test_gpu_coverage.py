@@ -1,0 +1,269 @@
+"""GPU parity, second part: rows whose weights cancel, the ntok 1..8 matrix
+on every tile height and segment length, sets up to 16 members, the
+invariants of the product, the workspace, and the two large workloads
+(the 202,048-row Q6_K matvec and the 52-layer Q/K/V/gate stream) checked
+row by row at full size.
+
+Every case runs through the C ABI and is compared with the binary64 oracle
+per row, |y_gpu - y_ref| <= 1e-4 * sum_j|W_ij x_j| + 1e-6; where the
+library promises equal bits (a set and its single calls, a token plane and
+the call with fewer planes of the same plan, scaled inputs, permuted rows)
+the bits are compared.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import kqgen
+import oracle
+import quant_matvec_amd as kq
+from cancel_blocks import cancel_weights
+from gpu_util import check_tol, dev, gpu_matvec, host, note, torch
+from kqgen import FORMATS, Q4_K, Q5_K, Q6_K
+from kqgen import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+NTHREADS = max(1, min(16, os.cpu_count() or 1))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    t = torch()
+    if not t.cuda.is_available():
+        pytest.skip("no GPU")
+    kq.load()
+    oracle.lib()
+
+
+def _bits(a):
+    return np.ascontiguousarray(a, np.float32).view(np.uint32)
+
+
+def _mm(entry, fmt, w, rows, cols, x):
+    """kq_matvec16 / kq_matmul on host arrays; y [ntok, rows]."""
+    t = torch()
+    x = np.atleast_2d(x).astype(np.float32)
+    y = t.full((x.shape[0], rows), float("nan"), dtype=t.float32, device="cuda")
+    getattr(kq, entry)(fmt, dev(w.reshape(-1)), rows, cols, dev(x), y, ntok=x.shape[0])
+    return host(y)
+
+
+def _run(entry, fmt, w, rows, cols, x):
+    if entry == "kq_matvec":
+        return gpu_matvec(fmt, w, rows, cols, x)
+    return _mm(entry, fmt, w, rows, cols, x)
+
+
+# ---- rows whose weights cancel (Ch 13 section 13.4.2: the single-rounding
+# form; the weights are exactly zero except a fraction of elements)
+
+CANCEL_CASES = [("kq_matvec", 1, 200), ("kq_matvec", 8, 200), ("kq_matvec", 1, 1100), ("kq_matvec", 2, 1100),
+                ("kq_matvec16", 16, 200), ("kq_matmul", 64, 200)]
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("frac", [0.0, 0.01, 0.05])
+@pytest.mark.parametrize("entry,ntok,rows", CANCEL_CASES)
+def test_cancelling_rows(fmt, frac, entry, ntok, rows):
+    cols = 6656
+    w = cancel_weights(fmt, rows, cols, frac, 11, rows)
+    x = kqgen.activations(ntok, cols, 996, fmt, ntok)
+    note("cancelling rows %s fmt=%d frac=%g %dx%d ntok=%d" % (entry, fmt, frac, rows, cols, ntok))
+    y = _run(entry, fmt, w, rows, cols, x)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=NTHREADS)
+    check_tol(y, y_ref, s, "cancelling %s fmt %d frac %g" % (entry, fmt, frac))
+    if frac == 0.0:
+        assert not y.any()                       # every weight is exactly zero
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("frac", [0.0, 0.02])
+def test_cancelling_rows_in_a_set(fmt, frac):
+    """A Q/K/V/gate-shaped set whose members cancel, through kq_matvec_set:
+    within tolerance and bitwise equal to the single calls."""
+    cols = 6656
+    specs = [(Q4_K, 4096), (Q6_K, 256), (fmt, 256), (Q5_K, 1100)]
+    ws = [cancel_weights(f, r, cols, frac, 12, i) for i, (f, r) in enumerate(specs)]
+    x = kqgen.activations(1, cols, 997, fmt)
+    note("cancelling set fmt=%d frac=%g" % (fmt, frac))
+    t = torch()
+    dx = dev(x)
+    ys = [t.full((1, r), float("nan"), dtype=t.float32, device="cuda") for (_, r) in specs]
+    kq.kq_matvec_set([dict(fmt=f, w=dev(w.reshape(-1)), x=dx, y=y, rows=r, cols=cols)
+                      for (f, r), w, y in zip(specs, ws, ys)])
+    for (f, r), w, y in zip(specs, ws, ys):
+        yh = host(y)
+        y_ref, s = oracle.matvec(f, w, r, cols, x, nthreads=NTHREADS)
+        check_tol(yh, y_ref, s, "cancelling set member fmt %d rows %d" % (f, r))
+        assert np.array_equal(_bits(yh), _bits(gpu_matvec(f, w, r, cols, x)))
+
+
+# ---- ntok 1..8 on every plan: 64-row tiles with one- and two-block
+# segments, 32-row tiles with two- and four-block segments.  Planes of
+# calls that plan the tensor alike are bitwise equal.
+
+# (rows, cols) -> groups of ntok that share one plan for every format
+NTOK_SHAPES = {
+    (131, 6656): [list(range(1, 9))],          # 64-row tiles, one-block segments
+    (1100, 2304): [list(range(1, 9))],         # odd blocks a row: 64-row tiles, two-block (Q6_K one-block)
+    (1100, 2560): [list(range(1, 9))],         # 32-row tiles at ntok 1-2, 64-row at 3-8, two-block segments
+    (1100, 6656): [[1, 2], list(range(3, 9))],  # 32-row four-block at ntok 1-2; 64-row two-block at 3-8
+}
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("shape", list(NTOK_SHAPES))
+def test_ntok_1_to_8_every_plan(fmt, shape):
+    rows, cols = shape
+    w = kqgen.weights(fmt, rows, cols, 640, fmt, rows, cols)
+    x = kqgen.activations(8, cols, 641, rows, cols)
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=NTHREADS)
+    ys = {}
+    for ntok in range(1, 9):
+        note("ntok matrix fmt=%d %dx%d ntok=%d" % (fmt, rows, cols, ntok))
+        ys[ntok] = gpu_matvec(fmt, w, rows, cols, x[:ntok], ldx=cols + 4, ldy=rows + 1)
+        check_tol(ys[ntok], y_ref[:ntok], s[:ntok], "fmt %d %dx%d ntok %d" % (fmt, rows, cols, ntok))
+    for group in NTOK_SHAPES[shape]:
+        top = max(group)
+        for ntok in group:
+            assert np.array_equal(_bits(ys[ntok]), _bits(ys[top][:ntok])), (ntok, top)
+
+
+@pytest.mark.parametrize("swapped", [False, True])
+def test_kv_pair_every_ntok_set_equals_singles(swapped):
+    """The mixed Q6_K/Q5_K K/V pair (separate x planes) at ntok 1..8: the set
+    launch bitwise equal to each tensor's own call, within tolerance."""
+    tensors = wl.kv_pair(swapped=swapped)[0]
+    t = torch()
+    ws = {T.name: kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey) for T in tensors}
+    for ntok in range(1, 9):
+        xs = {T.xkey: kqgen.activations(ntok, T.cols, *T.xkey) for T in tensors}
+        note("kv pair every ntok swapped=%s ntok=%d" % (swapped, ntok))
+        ys = {T.name: t.full((ntok, T.rows), float("nan"), dtype=t.float32, device="cuda") for T in tensors}
+        kq.kq_matvec_set([dict(fmt=T.fmt, w=dev(ws[T.name].reshape(-1)), x=dev(xs[T.xkey]), y=ys[T.name],
+                               rows=T.rows, cols=T.cols) for T in tensors], ntok=ntok)
+        for T in tensors:
+            y = host(ys[T.name])
+            y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey])
+            check_tol(y, y_ref, s, "pair %s ntok %d" % (T.name, ntok))
+            single = gpu_matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey])
+            assert np.array_equal(_bits(single), _bits(y)), (T.name, ntok)
+
+
+# (fmt, rows, cols, x index): every plan, shared and separate x planes
+SET16 = [(Q4_K, 4096, 6656, 0), (Q4_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0), (Q6_K, 256, 6656, 0),
+         (Q5_K, 1100, 2560, 1), (Q6_K, 1100, 2304, 1), (Q4_K, 300, 768, 2), (Q5_K, 64, 256, 2),
+         (Q6_K, 2000, 6656, 3), (Q4_K, 130, 19968, 4), (Q5_K, 17, 1024, 5), (Q6_K, 16448, 512, 6),
+         (Q4_K, 1, 256, 7), (Q5_K, 4100, 6656, 0), (Q6_K, 513, 2560, 1), (Q4_K, 2050, 5120, 8)]
+
+
+@pytest.mark.parametrize("ntok", [1, 2, 5])
+def test_sixteen_member_set(ntok):
+    t = torch()
+    xcols = {}
+    for f, r, c, xi in SET16:
+        xcols[xi] = max(c, xcols.get(xi, 0))      # a shared plane is as wide as its widest reader
+    xs = {xi: kqgen.activations(ntok, c, 650, xi, ntok) for xi, c in xcols.items()}
+    dxs = {xi: dev(v) for xi, v in xs.items()}
+    ws = [kqgen.weights(f, r, c, 651, i) for i, (f, r, c, _) in enumerate(SET16)]
+    ys = [t.full((ntok, r), float("nan"), dtype=t.float32, device="cuda") for (_, r, _, _) in SET16]
+    note("sixteen-member set ntok=%d" % ntok)
+    kq.kq_matvec_set([dict(fmt=f, w=dev(w.reshape(-1)), x=dxs[xi], y=y, rows=r, cols=c, ldx=xcols[xi])
+                      for (f, r, c, xi), w, y in zip(SET16, ws, ys)], ntok=ntok)
+    for i, ((f, r, c, xi), w, y) in enumerate(zip(SET16, ws, ys)):
+        yh = host(y)
+        x = np.ascontiguousarray(xs[xi][:, :c])
+        y_ref, s = oracle.matvec(f, w, r, c, x, nthreads=NTHREADS)
+        check_tol(yh, y_ref, s, "set16 member %d fmt %d %dx%d" % (i, f, r, c))
+        assert np.array_equal(_bits(yh), _bits(gpu_matvec(f, w, r, c, x, ldx=xcols[xi]))), i
+
+
+# ---- invariants: y(2^k x) = 2^k y bitwise (every rounding scales with x);
+# permuting the rows of W permutes y bitwise (a row's result does not
+# depend on where the row sits)
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("entry,ntok", [("kq_matvec", 1), ("kq_matvec", 4), ("kq_matvec16", 16), ("kq_matmul", 40)])
+def test_power_of_two_scaling_bitwise(fmt, entry, ntok):
+    rows, cols = 1100, 6656
+    w = kqgen.weights(fmt, rows, cols, 660, fmt)
+    x = kqgen.activations(ntok, cols, 661, fmt, ntok)
+    note("scaling %s fmt=%d ntok=%d" % (entry, fmt, ntok))
+    y = _run(entry, fmt, w, rows, cols, x)
+    for k in (5, -7):
+        yk = _run(entry, fmt, w, rows, cols, (x * np.float32(2.0 ** k)).astype(np.float32))
+        assert np.array_equal(_bits(yk), _bits((y * np.float32(2.0 ** k)).astype(np.float32))), k
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("entry,ntok", [("kq_matvec", 1), ("kq_matvec", 3), ("kq_matvec16", 16), ("kq_matmul", 40)])
+def test_row_permutation_bitwise(fmt, entry, ntok):
+    rows, cols = 1100, 6656
+    w = kqgen.weights(fmt, rows, cols, 662, fmt)
+    x = kqgen.activations(ntok, cols, 663, fmt, ntok)
+    perm = np.random.default_rng(664).permutation(rows)
+    note("row permutation %s fmt=%d ntok=%d" % (entry, fmt, ntok))
+    y = _run(entry, fmt, w, rows, cols, x)
+    yp = _run(entry, fmt, np.ascontiguousarray(w[perm]), rows, cols, x)
+    assert np.array_equal(_bits(yp), _bits(y[:, perm]))
+
+
+# ---- the workspace: freed and taken afresh, and grown past its first size
+# without a synchronizing call in between
+
+def test_workspace_release_and_regrow():
+    fmt, rows, cols = Q4_K, 4100, 6656
+    w = kqgen.weights(fmt, rows, cols, 670)
+    x = kqgen.activations(2, cols, 671)
+    note("workspace release")
+    y1 = gpu_matvec(fmt, w, rows, cols, x)
+    torch().cuda.synchronize()
+    kq.kq_release_workspace()
+    y2 = gpu_matvec(fmt, w, rows, cols, x)
+    assert np.array_equal(_bits(y1), _bits(y2))
+    # 8 token planes of a 19,200 x 65,536 Q4_K matrix take about 79 MB of
+    # shared-tile sums, more than the first workspace holds
+    rows, cols, ntok = 19200, 65536, 8
+    w = kqgen.weights(fmt, rows, cols, 672)
+    x = kqgen.activations(ntok, cols, 673)
+    note("workspace growth: Q4_K %dx%d ntok=%d" % (rows, cols, ntok))
+    ya = gpu_matvec(fmt, w, rows, cols, x)
+    yb = gpu_matvec(fmt, w, rows, cols, x)
+    assert np.array_equal(_bits(ya), _bits(yb))
+    idx = np.unique(np.concatenate([np.arange(0, 70), np.arange(rows - 70, rows),
+                                    np.random.default_rng(674).integers(0, rows, 300)]))
+    y_ref, s = oracle.matvec(fmt, w, rows, cols, x, row_idx=idx, nthreads=NTHREADS)
+    check_tol(ya[:, idx], y_ref, s, "workspace growth")
+
+
+# ---- the large workloads at full size, every row
+
+def test_lm_head_scale_q6k_all_rows():
+    """All 202,048 rows of the 202,048 x 6656 Q6_K matvec, in the launch the
+    benchmark times, against the multithreaded oracle."""
+    [[T]] = wl.lm_head()
+    w = kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey)
+    x = kqgen.activations(1, T.cols, *T.xkey)
+    note("lm_head Q6_K 202048x6656 all rows")
+    y = gpu_matvec(T.fmt, w, T.rows, T.cols, x)
+    y_ref, s = oracle.matvec(T.fmt, w, T.rows, T.cols, x, nthreads=NTHREADS)
+    check_tol(y, y_ref, s, "lm_head all rows")
+
+
+def test_stream52_all_layers_all_rows():
+    """All 52 layers of the Q/K/V/gate stream (one set launch per layer, as
+    the benchmark runs them), every row of every tensor."""
+    t = torch()
+    for li, tensors in enumerate(wl.qkvg_stream()):
+        ws = {T.name: kqgen.weights(T.fmt, T.rows, T.cols, *T.wkey) for T in tensors}
+        xs = {T.xkey: kqgen.activations(1, T.cols, *T.xkey) for T in tensors}
+        dx = {k: dev(v) for k, v in xs.items()}
+        ys = {T.name: t.full((1, T.rows), float("nan"), dtype=t.float32, device="cuda") for T in tensors}
+        note("stream layer %d" % li)
+        kq.kq_matvec_set([dict(fmt=T.fmt, w=dev(ws[T.name].reshape(-1)), x=dx[T.xkey], y=ys[T.name],
+                               rows=T.rows, cols=T.cols) for T in tensors])
+        for T in tensors:
+            y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey], nthreads=NTHREADS)
+            check_tol(host(ys[T.name]), y_ref, s, "stream layer %d %s" % (li, T.name))
