@@ -70,7 +70,8 @@ enum kq_status {
     KQ_ERR_OVERLAP = -8,   /* an output range overlaps another output or an input */
     KQ_ERR_SET_SIZE = -9,  /* n outside 1..KQ_MAX_SET */
     KQ_ERR_HIP = -10,      /* the HIP runtime reported an error */
-    KQ_ERR_TOO_LARGE = -11 /* a size exceeds the kernels' 32-bit index space */
+    KQ_ERR_TOO_LARGE = -11, /* a size exceeds the kernels' 32-bit index space */
+    KQ_ERR_SCRATCH = -12    /* kq_matvec_set_noalloc: the plan needs more than its fixed scratch */
 };
 
 #define KQ_MAX_SET 16
@@ -122,6 +123,22 @@ int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols,
  * n in 1..KQ_MAX_SET, ntok in 1..8 (common to the set).
  */
 int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream);
+
+/*
+ * kq_matvec_set for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, checks, results (bitwise equal to kq_matvec_set) and errors,
+ * but it allocates nothing, not even on its first call: the partial sums of
+ * tiles split between workgroups go to a fixed scratch array in device
+ * memory that the library holds on every GPU it runs on until the process
+ * ends (16 MB of sums and 65,536 counters).  A plan that needs more returns
+ * KQ_ERR_SCRATCH before any HIP call that enqueues work; decode sets of a
+ * model layer at ntok 1..8 and the 202,048-row matvec at ntok 1..2 fit.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on one
+ * GPU (on different streams, or from different threads) race.  The first
+ * call on a device enqueues a fill of the scratch's counters on `stream`.
+ */
+int kq_matvec_set_noalloc(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream);
 
 /*
  * Frees the workspaces kq_matvec / kq_matvec_set hold for `stream` on the

@@ -20,9 +20,10 @@ KQ_MAX_NTOK = 8
 STATUS = {
     0: "KQ_OK", -1: "KQ_ERR_FORMAT", -2: "KQ_ERR_COLS", -3: "KQ_ERR_ROWS", -4: "KQ_ERR_NTOK",
     -5: "KQ_ERR_NULL", -6: "KQ_ERR_ALIGN", -7: "KQ_ERR_STRIDE", -8: "KQ_ERR_OVERLAP",
-    -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE",
+    -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE", -12: "KQ_ERR_SCRATCH",
 }
-EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_validate_set", "kq_release_workspace",
+EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_matvec_set_noalloc",
+           "kq_validate_set", "kq_release_workspace",
            "kq_matvec16", "kq_matmul", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
            "kq_version")
 
@@ -60,6 +61,8 @@ def load() -> ctypes.CDLL:
         L.kq_matvec_set.restype = ctypes.c_int
         L.kq_validate_set.argtypes = [ctypes.POINTER(kq_tensor), i32, i32]
         L.kq_validate_set.restype = ctypes.c_int
+        L.kq_matvec_set_noalloc.argtypes = [ctypes.POINTER(kq_tensor), i32, i32, vp]
+        L.kq_matvec_set_noalloc.restype = ctypes.c_int
         L.kq_release_workspace.argtypes = [vp]
         L.kq_release_workspace.restype = ctypes.c_int
         L.kq_unpack_blocks.argtypes = [i32, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -177,6 +180,15 @@ def kq_validate_set(tensors, ntok: int = 1, n: int | None = None) -> int:
     arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
     count = len(arr) if n is None else n
     return load().kq_validate_set(arr, count, ntok)
+
+
+def kq_matvec_set_noalloc(tensors, ntok: int = 1, stream=None, n: int | None = None) -> None:
+    """kq_matvec_set with the library's fixed scratch instead of a workspace:
+    allocates nothing (raises KqError with KQ_ERR_SCRATCH for a plan that
+    needs more than the scratch holds)."""
+    arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
+    count = len(arr) if n is None else n
+    _check(load().kq_matvec_set_noalloc(arr, count, ntok, _stream(stream)), "kq_matvec_set_noalloc")
 
 
 def kq_release_workspace(stream=None) -> None:

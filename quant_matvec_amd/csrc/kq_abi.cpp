@@ -16,6 +16,7 @@ namespace kq {
 int launch_matvec(const KqLaunch& L, hipStream_t stream);
 int launch_capacity(int32_t ntok, int32_t lds_bytes);
 int launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
+int scratch_workspace(hipStream_t stream, size_t floats, size_t counters, float** partials, uint32_t** ctrs);
 int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,
                   int32_t* mins, float* d, float* dmin, hipStream_t stream);
@@ -391,6 +392,23 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
 
 int kq_release_workspace(void* stream) { return release_workspace(static_cast<hipStream_t>(stream)); }
 
+int kq_matvec_set_noalloc(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream) {
+    int rc = validate_set(tensors, n, ntok);
+    if (rc != KQ_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    KqLaunch L;
+    build_launch(tensors, n, ntok, &L);
+    const int cap = launch_capacity(ntok, L.lds_bytes);
+    if (cap <= 0) return KQ_ERR_HIP;
+    const KqPlanSizes sz = assign_workgroups(&L, cap);
+    float* partials = nullptr;
+    uint32_t* counters = nullptr;
+    rc = scratch_workspace(s, sz.partial_floats, sz.counters, &partials, &counters);
+    if (rc != KQ_OK) return rc;
+    bind_workspace(&L, partials, counters);
+    return launch_matvec(L, s);
+}
+
 int kq_matvec(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx,
               float* y, int64_t ldy, int32_t ntok, void* stream) {
     kq_tensor t;
@@ -508,6 +526,9 @@ const char* kq_strerror(int code) {
     case KQ_ERR_SET_SIZE: return "set size must be in 1..16";
     case KQ_ERR_HIP: return "HIP runtime error";
     case KQ_ERR_TOO_LARGE: return "size exceeds the kernels' index space";
+    case KQ_ERR_SCRATCH:
+        return "the plan needs more shared-tile sums than kq_matvec_set_noalloc's fixed scratch holds "
+               "(16 MB of sums, 65,536 counters); use kq_matvec_set";
     default: return "unknown status";
     }
 }

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kq_decode.h"
 #include "kq_plan.h"
 
@@ -1645,6 +1647,49 @@ int launch_zero(uint32_t* p, int64_t n, hipStream_t stream) {
     if (n <= 0) return KQ_OK;
     hipLaunchKernelGGL(kq_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+}
+
+// ------------------------------------------------------------ scratch of the allocation-free set call
+// kq_matvec_set_noalloc takes its shared-tile sums and arrival counters from
+// this array instead of a workspace it allocates.  Every call on a GPU uses
+// that GPU's copy of the array, so calls that overlap on one GPU race.  In
+// host code the array's name is a stand-in, not a device address: set-up
+// takes each device's address once with hipGetSymbolAddress (with that
+// device current), and only that address reaches kernels.
+constexpr size_t kScratchFloats = (size_t)4 << 20;         // 16 MB of shared-tile sums
+constexpr size_t kScratchCounters = (size_t)1 << 16;       // 65,536 arrival counters
+constexpr size_t kScratchBytes = kScratchFloats * sizeof(float) + kScratchCounters * sizeof(uint32_t);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mutex;
+static void* g_scratch_addr[16];                            // per device, set once
+
+// The scratch's sums and counters on the current device for a plan that
+// needs `floats` sums and `counters` counters; KQ_ERR_SCRATCH when that is
+// more than the array holds.  The first call on a device takes the array's
+// address and zeroes its counters with a fill kernel on `stream` (every
+// launch leaves the counters it used at zero again).  Allocates nothing.
+int scratch_workspace(hipStream_t stream, size_t floats, size_t counters, float** partials, uint32_t** ctrs) {
+    *partials = nullptr;
+    *ctrs = nullptr;
+    if (floats > kScratchFloats || counters > kScratchCounters) return KQ_ERR_SCRATCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return KQ_ERR_HIP;
+    void* base = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        if (g_scratch_addr[dev] == nullptr) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return KQ_ERR_HIP;
+            uint32_t* c = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p) + kScratchFloats * sizeof(float));
+            if (launch_zero(c, (int64_t)kScratchCounters, stream) != KQ_OK) return KQ_ERR_HIP;
+            g_scratch_addr[dev] = p;
+        }
+        base = g_scratch_addr[dev];
+    }
+    *partials = static_cast<float*>(base);
+    *ctrs = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + kScratchFloats * sizeof(float));
+    return KQ_OK;
 }
 
 int launch_unpack(int32_t fmt, const void* w, int64_t nblocks, int32_t* codes, int32_t* scales,

@@ -44,7 +44,7 @@ def test_version_and_geometry(lib):
     assert lib.kq_block_bytes(2) == -1
     assert lib.kq_row_bytes(12, 300) == -2
     assert lib.kq_row_bytes(99, 256) == -1
-    for code in range(-11, 1):
+    for code in range(-12, 1):
         assert kq.kq_strerror(code)
 
 
@@ -104,6 +104,9 @@ def test_invalid_calls_fail_before_hip(lib):
     assert lib.kq_matvec(13, BASE + 1, 256, 6656, BASE + (1 << 30), 6656, BASE + (2 << 30), 256, 1, None) == -6
     arr = kq.make_set([one()])
     assert lib.kq_matvec_set(arr, 0, 1, None) == -9
+    assert lib.kq_matvec_set_noalloc(arr, 0, 1, None) == -9
+    assert lib.kq_matvec_set_noalloc(arr, 1, 9, None) == -4
+    assert lib.kq_matvec_set_noalloc(kq.make_set([one(y=BASE + 64)]), 1, 1, None) == -8
     assert lib.kq_unpack_blocks(7, BASE, 1, None, None, None, None, None, None) == -1
     assert lib.kq_unpack_blocks(12, BASE, 0, None, None, None, None, None, None) == -3
     assert lib.kq_unpack_blocks(12, BASE + 4, 1, None, None, None, None, None, None) == -6
