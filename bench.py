@@ -67,7 +67,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-configs", action="store_true",
                    help="skip the per-configuration figures and the read calibration")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                    help="only run a plain device-to-device copy of BYTES bytes (counter calibration) and exit")
     return p.parse_args()
@@ -114,11 +114,11 @@ def main():
     r = run_workload(launches, wname, ntok, args.steps, args.warmup, dev, keep_host=not args.no_cpu_baseline)
     n_launch = r["launches"]
     bytes_per_launch = r["algo_bytes"] / n_launch
-    achieved_gbs = bytes_per_launch / (r["us_per_launch_kernel"] * 1e-6) / 1e9
+    achieved_gbs = bytes_per_launch / (r["us_per_launch_events"] * 1e-6) / 1e9
     value = r["weight_bytes"] * args.steps / r["elapsed"] / 1e9
     ms_per_step = r["elapsed"] / args.steps * 1e3
     weight_bytes = r["weight_bytes"]
-    avg_launch_us = r["us_per_launch_kernel"]
+    avg_launch_us = r["us_per_launch_events"]
 
     others = None
     if args.workload == "stream52" and not args.no_other_configs:
@@ -144,10 +144,10 @@ def main():
         "config": {"workload": wname, "launches_per_step": n_launch, "weight_bytes_per_step": weight_bytes,
                    "ntok": ntok, "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
                    "us_per_launch_end_to_end": round(ms_per_step * 1e3 / n_launch, 3),
-                   "us_per_launch_kernel": round(avg_launch_us, 3)},
+                   "us_per_launch_events": round(avg_launch_us, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wname),
-                     "kernel": "kq_matvec_kernel<1>", "bytes_per_launch": int(bytes_per_launch)},
+                     "kernel": r["kernel"], "bytes_per_launch": int(bytes_per_launch)},
         "cpu_baseline": cpu,
     }
     if others is not None:
@@ -194,6 +194,7 @@ def run_workload(launches, wname, ntok, steps, warmup, dev, keep_host=False):
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     n_launch = len(sets)
+    kernels = sorted({kq.kq_debug_plan_kernel(s, ntok=ntok) for s in sets})
 
     def step():
         for s in sets:
@@ -219,7 +220,8 @@ def run_workload(launches, wname, ntok, steps, warmup, dev, keep_host=False):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     return {"launches": n_launch, "weight_bytes": weight_bytes, "algo_bytes": algo_bytes, "elapsed": elapsed,
-            "us_per_launch_kernel": ev0.elapsed_time(ev1) * 1e3 / (steps * n_launch), "host": host}
+            "us_per_launch_events": ev0.elapsed_time(ev1) * 1e3 / (steps * n_launch), "host": host,
+            "kernel": "+".join(kernels)}
 
 
 def other_configs(dev):
@@ -237,7 +239,7 @@ def other_configs(dev):
 
     def one(key, launches, name, ntok, steps, warmup):
         r = run_workload(launches, name, ntok, steps, warmup, dev)
-        us = r["us_per_launch_kernel"]
+        us = r["us_per_launch_events"]
         res[key] = {"workload": name, "us_per_launch": round(us, 3),
                     "weight_GBs": round(r["weight_bytes"] / r["launches"] / (us * 1e-6) / 1e9, 1)}
 
@@ -427,29 +429,48 @@ def embedding_configs(dev):
     return out_res
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(host, ntok, budget_s):
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    whole tensors in launch order, wrapping around, until about budget_s
-    seconds of oracle time."""
+    """The CPU oracle (as it stands, untuned) on a bounded sample of the same
+    workload: whole tensors in launch order, wrapping around, timed twice --
+    on one thread for about a third of budget_s, then split over rows on
+    every CPU this process may run on for the rest.  `value` is the all-core
+    rate; the one-thread rate, nproc and the CPU model ride along."""
     import oracle
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count() or 1
-    threads = max(1, min(threads, 16))
-    done_bytes = 0
-    spent = 0.0
-    tensors = 0
-    while spent < budget_s:
-        for T, w, x in host:
-            t0 = time.perf_counter()
-            oracle.matvec(T.fmt, w, T.rows, T.cols, x, nthreads=threads)
-            spent += time.perf_counter() - t0
-            done_bytes += T.weight_bytes
-            tensors += 1
-            if spent >= budget_s:
-                break
-    return {"value": round(done_bytes / spent / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d whole tensors (%d weight bytes) of the same workload in launch order, ntok=%d, %.1f s"
-                      % (tensors, done_bytes, ntok, spent)}
+    def run(threads, seconds):
+        done_bytes, spent, tensors = 0, 0.0, 0
+        while spent < seconds:
+            for T, w, x in host:
+                t0 = time.perf_counter()
+                oracle.matvec(T.fmt, w, T.rows, T.cols, x, nthreads=threads)
+                spent += time.perf_counter() - t0
+                done_bytes += T.weight_bytes
+                tensors += 1
+                if spent >= seconds:
+                    break
+        return done_bytes, spent, tensors
+
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:
+        ncpu = os.cpu_count() or 1
+    b1, s1, n1 = run(1, budget_s / 3.0)
+    bn, sn, nn = run(ncpu, budget_s * 2.0 / 3.0)
+    return {"value": round(bn / sn / 1e9, 4), "unit": "GB/s", "cores": ncpu, "kind": "oracle",
+            "sample": "%d whole tensors (%d weight bytes) of the same workload in launch order, ntok=%d, %.1f s "
+                      "on %d threads; one thread: %d tensors (%d bytes) in %.1f s" % (nn, bn, ntok, sn, ncpu, n1, b1, s1),
+            "single_thread_value": round(b1 / s1 / 1e9, 4), "nproc": os.cpu_count(), "cpu_model": _cpu_model()}
 
 
 def copy_calibration(nbytes, dev):

@@ -254,6 +254,25 @@ int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols,
  */
 int kq_debug_read_probe(const void* buf, int64_t bytes, void* sink, void* stream);
 
+/*
+ * Debug/test export: on = 0 makes kq_matvec, kq_matvec_set and
+ * kq_matvec_set_noalloc use only the one-wave-workgroup kernel; on = 1
+ * (the default, unless the environment sets KQMV_PIPELINE=0) lets launches
+ * whose tensors all run in 32-row tiles at ntok <= 2 take the pipelined
+ * producer/consumer kernel.  Both give the same bits.  Process-wide; not
+ * for use while other threads launch.  Returns KQ_OK.
+ */
+int kq_debug_set_pipeline(int32_t on);
+
+/*
+ * Debug/test export: which kernel kq_matvec_set would launch for this set
+ * on the current device: 1 the pipelined producer/consumer kernel, 0 the
+ * one-wave-workgroup kernel, or a negative KQ_ERR_* code if the set is
+ * invalid (the kq_validate_set checks).  Launches nothing; reads only the
+ * descriptors (not the buffers they point to).
+ */
+int kq_debug_plan_kernel(const kq_tensor* tensors, int32_t n, int32_t ntok);
+
 /* Static description of a status code (never NULL). */
 const char* kq_strerror(int code);
 

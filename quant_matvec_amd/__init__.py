@@ -23,7 +23,7 @@ STATUS = {
     -9: "KQ_ERR_SET_SIZE", -10: "KQ_ERR_HIP", -11: "KQ_ERR_TOO_LARGE", -12: "KQ_ERR_SCRATCH",
 }
 EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_matvec_set_noalloc",
-           "kq_validate_set", "kq_release_workspace",
+           "kq_validate_set", "kq_release_workspace", "kq_debug_set_pipeline", "kq_debug_plan_kernel",
            "kq_matvec16", "kq_matmul", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
            "kq_version")
 
@@ -63,6 +63,10 @@ def load() -> ctypes.CDLL:
         L.kq_validate_set.restype = ctypes.c_int
         L.kq_matvec_set_noalloc.argtypes = [ctypes.POINTER(kq_tensor), i32, i32, vp]
         L.kq_matvec_set_noalloc.restype = ctypes.c_int
+        L.kq_debug_set_pipeline.argtypes = [i32]
+        L.kq_debug_set_pipeline.restype = ctypes.c_int
+        L.kq_debug_plan_kernel.argtypes = [ctypes.POINTER(kq_tensor), i32, i32]
+        L.kq_debug_plan_kernel.restype = ctypes.c_int
         L.kq_release_workspace.argtypes = [vp]
         L.kq_release_workspace.restype = ctypes.c_int
         L.kq_unpack_blocks.argtypes = [i32, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -189,6 +193,21 @@ def kq_matvec_set_noalloc(tensors, ntok: int = 1, stream=None, n: int | None = N
     arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
     count = len(arr) if n is None else n
     _check(load().kq_matvec_set_noalloc(arr, count, ntok, _stream(stream)), "kq_matvec_set_noalloc")
+
+
+def kq_debug_set_pipeline(on: bool) -> None:
+    """Debug/test: allow (True, the default) or forbid the pipelined kernel."""
+    _check(load().kq_debug_set_pipeline(1 if on else 0), "kq_debug_set_pipeline")
+
+
+def kq_debug_plan_kernel(tensors, ntok: int = 1, n: int | None = None) -> str:
+    """Debug/test: the kernel kq_matvec_set would launch for this set on the
+    current device, "kq_pc_kernel<ntok>" (pipelined) or "kq_matvec_kernel<ntok>"."""
+    arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
+    count = len(arr) if n is None else n
+    rc = load().kq_debug_plan_kernel(arr, count, ntok)
+    _check(rc, "kq_debug_plan_kernel")
+    return ("kq_pc_kernel<%d>" if rc == 1 else "kq_matvec_kernel<%d>") % ntok
 
 
 def kq_release_workspace(stream=None) -> None:

@@ -14,7 +14,9 @@
 namespace kq {
 
 int launch_matvec(const KqLaunch& L, hipStream_t stream);
-int launch_capacity(int32_t ntok, int32_t lds_bytes);
+int launch_capacity(const KqLaunch& L);
+int plan_pipelined(KqLaunch* L);
+void set_pipeline(int on);
 int launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
 int scratch_workspace(hipStream_t stream, size_t floats, size_t counters, float** partials, uint32_t** ctrs);
 int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
@@ -48,50 +50,26 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows) {
     return w + 1024 * ntok * (pair ? 2 : 1);
 }
 
-// Segment length S: 2 super-blocks, except for matrices whose workgroups
-// get few segments in any launch: any matrix of at most kTinyRows rows, and
-// a Q6_K matrix of at most kSmallRows rows with an odd number of blocks a
-// row, take 1; and long rows in 32-row tiles take 4 unless the matrix has
-// between kSmallRows and 4*kSmallRows rows.  A K/V-sized launch then splits
-// into one-block runs, a decode set into about one segment per resident
-// wave, while a large matrix keeps few partial sums.  Depends on the tensor's shape and, through the tile
-// height, on ntok; a set member's plan never depends on the other members.
-//
-// Tile rows: 32 for a matrix of more than kTinyRows rows and an even number
-// of blocks a row at one token plane (and at two up to kSmallRows rows),
-// else 64.  With 64-row tiles every wave of an XCD keeps the L2 lines its 64
-// rows share between successive block columns live, more than the L2 holds
-// on a large matrix, and about a third of the lines are read twice; 32-row
-// tiles that take a segment (two columns) a step halve that and stay near
-// one read per line.  With more token planes the compute per byte grows
-// and 64-row tiles are faster.  Both heights sum the same two-block segments
-// the same way, so where S is 2 in both a plane's result does not depend on
-// the height.
+// Tile rows and segment length S.  A matrix with an even number of blocks
+// a row runs in 32-row tiles at one token plane (and at two up to kSmallRows
+// rows) with two-block segments: two lanes a row, one segment a step, which
+// keeps the L2 lines shared by consecutive block columns of a row live for
+// only one step per wave, and lets the pipelined kernel take every decode
+// set and large matrix.  Otherwise 64-row tiles, one lane a row, with S = 1
+// for a matrix of at most kTinyRows rows (few segments a launch: one-block
+// runs keep its latency down) and for a Q6_K matrix of at most kSmallRows
+// rows with an odd number of blocks a row, else S = 2.  Both tile heights sum
+// two-block segments the same way, so where S is 2 at two token counts a
+// plane's result does not depend on the height.  Depends only on the
+// tensor's own (fmt, rows, cols) and ntok, never on the rest of a set.
 constexpr int64_t kSmallRows = 16384;
 constexpr int64_t kTinyRows = 1024;
-constexpr int64_t kLongRowBlocks = 20;
 void plan_tensor(int32_t fmt, int64_t rows, int64_t cols, int32_t ntok, int32_t* nseg, int32_t* seg,
                  int32_t* tile_rows) {
     const int64_t nb = cols / 256;
-    // A matrix of more than kTinyRows rows and an even number of blocks a row
-    // may run in 32-row tiles: at one token plane, and at two up to
-    // kSmallRows rows; with more planes the compute per byte grows and
-    // 64-row tiles run faster.
-    const bool pairable = rows > kTinyRows && nb % 2 == 0;
-    *tile_rows = pairable && (ntok == 1 || (ntok == 2 && rows <= kSmallRows)) ? 32 : kTileRows;
-    // In 32-row tiles a row of kLongRowBlocks blocks or more takes four-block
-    // segments (two steps) on a matrix of at most kSmallRows rows (a decode
-    // set then makes about one segment per resident wave) or of at least
-    // 4*kSmallRows (long runs of whole tiles, fewer partial sums).  In
-    // between (an FFN gate or up projection) four-block runs come out too
-    // coarse over the few segments each wave gets and measure slower.
-    // Otherwise a pairable matrix takes two-block segments in either tile
-    // height, so its planes sum alike at any ntok.
-    const bool long_seg = *tile_rows == 32 && nb >= kLongRowBlocks &&
-                          (rows <= kSmallRows || rows >= 4 * kSmallRows);
-    const int32_t S = long_seg ? 4
-                      : pairable ? 2
-                      : ((fmt == KQ_Q6_K && rows <= kSmallRows) || rows <= kTinyRows) ? 1 : 2;
+    const bool pair = nb % 2 == 0 && (ntok == 1 || (ntok == 2 && rows <= kSmallRows));
+    *tile_rows = pair ? 32 : kTileRows;
+    const int32_t S = pair ? 2 : ((fmt == KQ_Q6_K && rows <= kSmallRows && nb % 2) || rows <= kTinyRows) ? 1 : 2;
     *seg = S;
     *nseg = (int32_t)((nb + S - 1) / S);
 }
@@ -354,7 +332,8 @@ static int release_workspace(hipStream_t stream) {
 static int enqueue_set(const kq_tensor* tensors, int32_t n, int32_t ntok, hipStream_t s) {
     KqLaunch L;
     build_launch(tensors, n, ntok, &L);
-    const int cap = launch_capacity(ntok, L.lds_bytes);
+    plan_pipelined(&L);
+    const int cap = launch_capacity(L);
     if (cap <= 0) return KQ_ERR_HIP;
     const KqPlanSizes sz = assign_workgroups(&L, cap);
     float* partials = nullptr;
@@ -392,13 +371,28 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
 
 int kq_release_workspace(void* stream) { return release_workspace(static_cast<hipStream_t>(stream)); }
 
+int kq_debug_set_pipeline(int32_t on) {
+    set_pipeline(on);
+    return KQ_OK;
+}
+
+int kq_debug_plan_kernel(const kq_tensor* tensors, int32_t n, int32_t ntok) {
+    const int rc = validate_set(tensors, n, ntok);
+    if (rc != KQ_OK) return rc;
+    KqLaunch L;
+    build_launch(tensors, n, ntok, &L);
+    plan_pipelined(&L);
+    return L.pipelined ? 1 : 0;
+}
+
 int kq_matvec_set_noalloc(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream) {
     int rc = validate_set(tensors, n, ntok);
     if (rc != KQ_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     KqLaunch L;
     build_launch(tensors, n, ntok, &L);
-    const int cap = launch_capacity(ntok, L.lds_bytes);
+    plan_pipelined(&L);
+    const int cap = launch_capacity(L);
     if (cap <= 0) return KQ_ERR_HIP;
     const KqPlanSizes sz = assign_workgroups(&L, cap);
     float* partials = nullptr;

@@ -33,8 +33,10 @@
 //     contraction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "kq_decode.h"
 #include "kq_plan.h"
@@ -51,6 +53,9 @@ __device__ __forceinline__ gbytes_t gbytes(const void* p) { return (gbytes_t)(p)
 // the compiler wait for every load in flight after them.
 typedef __attribute__((address_space(1))) float* gfloat_t;
 __device__ __forceinline__ gfloat_t gfloat(float* p) { return (gfloat_t)(p); }
+
+// Lane within the wave (workgroups of the pipelined kernel hold ten waves).
+__device__ __forceinline__ int kq_lane() { return (int)(threadIdx.x & 63); }
 
 constexpr float kTwo24 = 16777216.0f;        // undoes the 2^-24 of a subnormal code
 constexpr float kTwo20 = 1048576.0f;         // ... of a high nibble left in place (16 * code * 2^-24)
@@ -102,6 +107,21 @@ __device__ __forceinline__ S load_uniform(const S& src) {
 __device__ __forceinline__ uint4 lds_read4(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t lds_read1(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
+// Direct global -> LDS loads (the pipelined kernel's producers): every lane
+// reads SIZE bytes at its own address g, and the wave's 64 pieces land
+// contiguously at lds + SIZE * lane (lds is the wave-uniform base).  They
+// count in vmcnt until the bytes are in LDS.
+template <int SIZE>
+__device__ __forceinline__ void dma(gbytes_t g, uint8_t* lds) {
+    static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte pieces");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                         (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+    else
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                         (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
 // ------------------------------------------------------------ x staging
 // The x values of one super-block column (1 KB per token plane) travel with
 // the weights: lane i loads x[4i..4i+3] of the next column into registers,
@@ -111,14 +131,14 @@ template <int NTOK>
 struct XStage {
     float4 v[NTOK];
     __device__ __forceinline__ void load(const KqDesc& T, int b) {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int t = 0; t < NTOK; ++t)
             v[t] = __builtin_bit_cast(float4, *(const __attribute__((address_space(1))) u32x4*)(
                                                   gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane)));
     }
     __device__ __forceinline__ void commit(uint8_t* xslot) const {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) reinterpret_cast<float4*>(xslot + 1024 * t)[lane] = v[t];
     }
@@ -164,15 +184,8 @@ struct K45 {
 // error is bounded by a multiple of sum_j |W_ij x_j| (no separate min term
 // that could cancel against the code term).
 template <int FMT, int NTOK, int G>
-__device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&qh)[8], const K4Scales& S, float d,
+__device__ __forceinline__ void k45_group(const uint32_t (&qs)[8], const uint32_t (&qh)[8], const K4Scales& S, float d,
                                           float dmin, const uint8_t* xslot, float (&c)[NTOK]) {
-    uint32_t qs[8];
-    {
-        const uint4 a = lds_read4(row + K45<FMT>::QS_OFF + 32 * G);
-        const uint4 b = lds_read4(row + K45<FMT>::QS_OFF + 32 * G + 16);
-        qs[0] = a.x; qs[1] = a.y; qs[2] = a.z; qs[3] = a.w;
-        qs[4] = b.x; qs[5] = b.y; qs[6] = b.z; qs[7] = b.w;
-    }
     const float a_lo = d * (float)k4_sc(S, 2 * G) * kTwo24;          // exact
     const float a_hi = d * (float)k4_sc(S, 2 * G + 1) * kTwo20;
     const float n_lo = -(dmin * (float)k4_m(S, 2 * G));               // exact
@@ -180,12 +193,12 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
     float al[NTOK], ah[NTOK];
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) { al[t] = 0.0f; ah[t] = 0.0f; }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
+    // The weights of step k (elements 64G + 4k + i and 64G + 32 + 4k + i),
+    // multiplied into al / ah with that step's x.
+    auto step = [&](int k, const float4 (&xl)[NTOK], const float4 (&xh)[NTOK]) {
         Packed4 p;
         if constexpr (FMT == KQ_Q4_K) p = k4_codes(qs[k]);
         else p = k5_codes<G>(qs[k], qh[k]);
-        const int e = 64 * G + 4 * k;
         const float wl0 = __builtin_fmaf(a_lo, (float)half_lo(p.lo02), n_lo);
         const float wl1 = __builtin_fmaf(a_lo, (float)half_lo(p.lo13), n_lo);
         const float wl2 = __builtin_fmaf(a_lo, (float)half_hi(p.lo02), n_lo);
@@ -196,24 +209,107 @@ __device__ __forceinline__ void k45_group(const uint8_t* row, const uint32_t (&q
         const float wh3 = __builtin_fmaf(a_hi, (float)half_hi(p.hi13), n_hi);
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) {
-            const float4 xl = xread(xslot, t, e), xh = xread(xslot, t, e + 32);
-            al[t] = __builtin_fmaf(wl0, xl.x, al[t]);
-            al[t] = __builtin_fmaf(wl1, xl.y, al[t]);
-            al[t] = __builtin_fmaf(wl2, xl.z, al[t]);
-            al[t] = __builtin_fmaf(wl3, xl.w, al[t]);
-            ah[t] = __builtin_fmaf(wh0, xh.x, ah[t]);
-            ah[t] = __builtin_fmaf(wh1, xh.y, ah[t]);
-            ah[t] = __builtin_fmaf(wh2, xh.z, ah[t]);
-            ah[t] = __builtin_fmaf(wh3, xh.w, ah[t]);
+            al[t] = __builtin_fmaf(wl0, xl[t].x, al[t]);
+            al[t] = __builtin_fmaf(wl1, xl[t].y, al[t]);
+            al[t] = __builtin_fmaf(wl2, xl[t].z, al[t]);
+            al[t] = __builtin_fmaf(wl3, xl[t].w, al[t]);
+            ah[t] = __builtin_fmaf(wh0, xh[t].x, ah[t]);
+            ah[t] = __builtin_fmaf(wh1, xh[t].y, ah[t]);
+            ah[t] = __builtin_fmaf(wh2, xh[t].z, ah[t]);
+            ah[t] = __builtin_fmaf(wh3, xh[t].w, ah[t]);
+        }
+    };
+    if constexpr (NTOK <= 2) {
+        // x of step k in buffer k % 2, read one step ahead; step_end keeps
+        // later reads from being hoisted (the registers of a whole group's
+        // x would not fit beside the rest)
+        float4 xb[2][2][NTOK];
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            xb[0][0][t] = xread(xslot, t, 64 * G);
+            xb[0][1][t] = xread(xslot, t, 64 * G + 32);
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k + 1 < 8) {
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) {
+                    xb[(k + 1) % 2][0][t] = xread(xslot, t, 64 * G + 4 * (k + 1));
+                    xb[(k + 1) % 2][1][t] = xread(xslot, t, 64 * G + 32 + 4 * (k + 1));
+                }
+            }
+            step(k, xb[k % 2][0], xb[k % 2][1]);
+            step_end<NTOK>(al, ah);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            Packed4 p;
+            if constexpr (FMT == KQ_Q4_K) p = k4_codes(qs[k]);
+            else p = k5_codes<G>(qs[k], qh[k]);
+            const int e = 64 * G + 4 * k;
+            const float wl0 = __builtin_fmaf(a_lo, (float)half_lo(p.lo02), n_lo);
+            const float wl1 = __builtin_fmaf(a_lo, (float)half_lo(p.lo13), n_lo);
+            const float wl2 = __builtin_fmaf(a_lo, (float)half_hi(p.lo02), n_lo);
+            const float wl3 = __builtin_fmaf(a_lo, (float)half_hi(p.lo13), n_lo);
+            const float wh0 = __builtin_fmaf(a_hi, (float)half_lo(p.hi02), n_hi);
+            const float wh1 = __builtin_fmaf(a_hi, (float)half_lo(p.hi13), n_hi);
+            const float wh2 = __builtin_fmaf(a_hi, (float)half_hi(p.hi02), n_hi);
+            const float wh3 = __builtin_fmaf(a_hi, (float)half_hi(p.hi13), n_hi);
+#pragma unroll
+            for (int t = 0; t < NTOK; ++t) {
+                const float4 xl = xread(xslot, t, e), xh = xread(xslot, t, e + 32);
+                al[t] = __builtin_fmaf(wl0, xl.x, al[t]);
+                al[t] = __builtin_fmaf(wl1, xl.y, al[t]);
+                al[t] = __builtin_fmaf(wl2, xl.z, al[t]);
+                al[t] = __builtin_fmaf(wl3, xl.w, al[t]);
+                ah[t] = __builtin_fmaf(wh0, xh.x, ah[t]);
+                ah[t] = __builtin_fmaf(wh1, xh.y, ah[t]);
+                ah[t] = __builtin_fmaf(wh2, xh.z, ah[t]);
+                ah[t] = __builtin_fmaf(wh3, xh.w, ah[t]);
+            }
         }
     }
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) c[t] = (c[t] + al[t]) + ah[t];
 }
 
+// The qs words of group G of a block at `row` (LDS).
+template <int FMT, int G>
+__device__ __forceinline__ void k45_qs(const uint8_t* row, uint32_t (&qs)[8]) {
+    const uint4 a = lds_read4(row + K45<FMT>::QS_OFF + 32 * G);
+    const uint4 b = lds_read4(row + K45<FMT>::QS_OFF + 32 * G + 16);
+    qs[0] = a.x; qs[1] = a.y; qs[2] = a.z; qs[3] = a.w;
+    qs[4] = b.x; qs[5] = b.y; qs[6] = b.z; qs[7] = b.w;
+}
+
+// The block's contribution from its header, qh words and the qs words of
+// each group (read by the caller into qs[G]), formed from zero (sub-blocks
+// 0..7 summed in order) and then added to acc, so that a block adds the
+// same bits in either tile height and from LDS or registers.
+template <int FMT, int NTOK, class QS>
+__device__ __forceinline__ void k45_block(const uint4& hdr, const uint32_t (&qh)[8], const QS& qs_of,
+                                          const uint8_t* xslot, float (&acc)[NTOK]) {
+    const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
+    const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
+    float c[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
+    uint32_t qs[8];
+    qs_of(qs, std::integral_constant<int, 0>());
+    k45_group<FMT, NTOK, 0>(qs, qh, S, d, dmin, xslot, c);
+    qs_of(qs, std::integral_constant<int, 1>());
+    k45_group<FMT, NTOK, 1>(qs, qh, S, d, dmin, xslot, c);
+    qs_of(qs, std::integral_constant<int, 2>());
+    k45_group<FMT, NTOK, 2>(qs, qh, S, d, dmin, xslot, c);
+    qs_of(qs, std::integral_constant<int, 3>());
+    k45_group<FMT, NTOK, 3>(qs, qh, S, d, dmin, xslot, c);
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
+}
+
 // acc[t] += the contribution of the Q4_K/Q5_K block at `row` (LDS) with x
-// at xslot, formed from zero (sub-blocks 0..7 summed in order) and then
-// added, so that a block adds the same bits in either tile height.
+// at xslot.
 template <int FMT, int NTOK>
 __device__ __forceinline__ void block_mac(const uint8_t* row, const uint8_t* xslot, float (&acc)[NTOK]) {
     const uint4 hdr = lds_read4(row);
@@ -226,17 +322,30 @@ __device__ __forceinline__ void block_mac(const uint8_t* row, const uint8_t* xsl
 #pragma unroll
         for (int i = 0; i < 8; ++i) qh[i] = 0;
     }
-    const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
-    const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-    float c[NTOK];
+    k45_block<FMT, NTOK>(hdr, qh, [&](uint32_t (&qs)[8], auto g) { k45_qs<FMT, decltype(g)::value>(row, qs); },
+                         xslot, acc);
+}
+
+// The same from the block's bytes held in registers (wv: the block's 16-byte
+// chunks, as it lies in memory).
+template <int FMT, int NTOK>
+__device__ __forceinline__ void block_mac_regs(const uint4 (&wv)[K45<FMT>::C], const uint8_t* xslot,
+                                               float (&acc)[NTOK]) {
+    uint32_t qh[8];
+    if constexpr (FMT == KQ_Q5_K) {
+        qh[0] = wv[1].x; qh[1] = wv[1].y; qh[2] = wv[1].z; qh[3] = wv[1].w;
+        qh[4] = wv[2].x; qh[5] = wv[2].y; qh[6] = wv[2].z; qh[7] = wv[2].w;
+    } else {
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t) c[t] = 0.0f;
-    k45_group<FMT, NTOK, 0>(row, qh, S, d, dmin, xslot, c);
-    k45_group<FMT, NTOK, 1>(row, qh, S, d, dmin, xslot, c);
-    k45_group<FMT, NTOK, 2>(row, qh, S, d, dmin, xslot, c);
-    k45_group<FMT, NTOK, 3>(row, qh, S, d, dmin, xslot, c);
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + c[t];
+        for (int i = 0; i < 8; ++i) qh[i] = 0;
+    }
+    constexpr int Q = K45<FMT>::QS_OFF / 16;
+    k45_block<FMT, NTOK>(wv[0], qh, [&](uint32_t (&qs)[8], auto g) {
+        constexpr int G = decltype(g)::value;
+        const uint4 a = wv[Q + 2 * G], b = wv[Q + 2 * G + 1];
+        qs[0] = a.x; qs[1] = a.y; qs[2] = a.z; qs[3] = a.w;
+        qs[4] = b.x; qs[5] = b.y; qs[6] = b.z; qs[7] = b.w;
+    }, xslot, acc);
 }
 
 // Per-lane staging offsets of a 64-row column: 16-byte chunk q = 64*i + lane
@@ -247,7 +356,7 @@ template <int C>
 struct K45Offsets {
     uint32_t off[C];
     __device__ __forceinline__ void init(const KqDesc& T) {
-        int lane = threadIdx.x;
+        int lane = kq_lane();
         // opaque to the optimizer, so these per-format offsets are formed
         // here and not hoisted to the kernel entry for every format
         asm volatile("" : "+v"(lane));
@@ -287,7 +396,7 @@ struct K45Column {
         xs.load(T, valid ? b : 0);
     }
     __device__ __forceinline__ void commit(uint8_t* slot) const {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int i = 0; i < C; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         xs.commit(slot + K45<FMT>::WSLOT);
@@ -298,7 +407,7 @@ struct K45Column {
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
                                                    float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
-        block_mac<FMT, NTOK>(slot + threadIdx.x * BB, slot + K45<FMT>::WSLOT, acc);
+        block_mac<FMT, NTOK>(slot + kq_lane() * BB, slot + K45<FMT>::WSLOT, acc);
     }
 };
 
@@ -316,7 +425,7 @@ struct K45Pair {
     struct Offsets {
         uint32_t off[N];
         __device__ __forceinline__ void init(const KqDesc& T) {
-            int lane = threadIdx.x;
+            int lane = kq_lane();
             asm volatile("" : "+v"(lane));
 #pragma unroll
             for (int i = 0; i < N; ++i) {
@@ -328,6 +437,39 @@ struct K45Pair {
     };
     uint4 stg[N];
     XStage<NTOK> xs0, xs1;
+    // ---- the pipelined kernel's pieces: the step's weights (in commit()'s
+    // layout, chunk q at byte 16q) and its x (block b, then b+1) go to
+    // separate LDS slots by direct loads; a consumer reads its lane's block
+    // into registers, frees the weight slot, and computes from registers
+    static constexpr int LOADS = N + 2 * NTOK;                 // direct loads of one step
+    static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
+    static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
+        const int rows_here = min(TR, T.rows - tile * TR);
+        const uint32_t max_off = (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C2 - 1);
+        gbytes_t col = gbytes(T.w) + (size_t)tile * TR * T.row_bytes + (size_t)b * BB;
+#pragma unroll
+        for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
+    }
+    static __device__ __forceinline__ void dma_x(const KqDesc& T, int b, uint8_t* xslot) {
+        const int lane = kq_lane();
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane), xslot + 1024 * t);
+            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (b + 1) + 4 * lane), xslot + 1024 * (NTOK + t));
+        }
+    }
+    struct Regs {
+        uint4 v[C];
+    };
+    static __device__ __forceinline__ void load_regs(const uint8_t* wslot, Regs& r) {
+        const int lane = kq_lane();
+        const uint8_t* blk = wslot + (lane >> 1) * 2 * BB + (lane & 1) * BB;
+#pragma unroll
+        for (int i = 0; i < C; ++i) r.v[i] = lds_read4(blk + 16 * i);
+    }
+    static __device__ __forceinline__ void compute_regs(const Regs& r, const uint8_t* xslot, float (&acc)[NTOK]) {
+        block_mac_regs<FMT, NTOK>(r.v, xslot + (kq_lane() & 1) * 1024 * NTOK, acc);
+    }
 
     // Branch-free, clamped like the 64-row column (rows past the tensor's
     // end read its last row's last chunk; `valid` false reads the tensor's
@@ -343,7 +485,7 @@ struct K45Pair {
         xs1.load(T, valid ? b + 1 : 1);
     }
     __device__ __forceinline__ void commit(uint8_t* slot) const {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         xs0.commit(slot + WSLOT);
@@ -352,7 +494,7 @@ struct K45Pair {
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
                                                    float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
-        const int lane = threadIdx.x, k = lane & 1;
+        const int lane = kq_lane(), k = lane & 1;
         block_mac<FMT, NTOK>(slot + (lane >> 1) * 2 * BB + k * BB, slot + WSLOT + k * 1024 * NTOK, acc);
     }
 };
@@ -397,12 +539,11 @@ constexpr uint32_t kQ6NegHi = 0x82008200u;    // -512 * 2^-24: the offset of a h
 // code carries its offset (q6_signed), so every rounding is relative to
 // |W_e x_e| and nothing is subtracted after the sum.
 template <int NTOK, int N, int KH>
-__device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, const uint32_t (&scw)[4],
-                                               const uint8_t* xslot, float (&tl)[NTOK], float (&th)[NTOK]) {
-    uint32_t A[4], B[4], H[4];
-    q6_read4(row, 16 * N + 4 * KH, sh, A);          // ql bytes 64N + 16KH ..
-    q6_read4(row, 16 * N + 8 + 4 * KH, sh, B);      // ql bytes 64N + 32 + 16KH ..
-    q6_read4(row, 32 + 8 * N + 4 * KH, sh, H);      // qh bytes 32N + 16KH ..
+__device__ __forceinline__ void q6_quarter_run(const uint32_t (&A)[4], const uint32_t (&B)[4], const uint32_t (&H)[4],
+                                               const uint32_t (&scw)[4], const uint8_t* xslot, float (&tl)[NTOK],
+                                               float (&th)[NTOK]) {
+    // A: ql bytes 64N + 16KH.., B: ql bytes 64N + 32 + 16KH.., H: qh bytes
+    // 32N + 16KH.. (realigned words)
     float a[4][NTOK];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
@@ -481,6 +622,39 @@ __device__ __forceinline__ void q6_quarter_run(const uint8_t* row, uint32_t sh, 
     }
 }
 
+// The Q6_K block's contribution from its scale words 48..51, word 52 (scales
+// 14-15 and d, or d alone) and, per quarter run (N, KH), the realigned ql
+// and qh words that words(N, KH, A, B, H) fetches; formed from zero and
+// then added to acc, so that a block adds the same bits in either tile
+// height and from LDS or registers.
+template <int NTOK, class W>
+__device__ __forceinline__ void q6_block(uint32_t s48, uint32_t s49, uint32_t s50, uint32_t s51, uint32_t w52,
+                                         uint32_t sh, const W& words, const uint8_t* xslot, float (&acc)[NTOK]) {
+    uint32_t scw[4];
+    scw[0] = __builtin_amdgcn_alignbit(s49, s48, sh);
+    scw[1] = __builtin_amdgcn_alignbit(s50, s49, sh);
+    scw[2] = __builtin_amdgcn_alignbit(s51, s50, sh);
+    scw[3] = __builtin_amdgcn_alignbit(w52, s51, sh);
+    const float d = f16_to_f32((w52 >> sh) & 0xFFFFu);
+    float tl[NTOK], th[NTOK];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
+    uint32_t A[4], B[4], H[4];
+    using Z = std::integral_constant<int, 0>;
+    using O = std::integral_constant<int, 1>;
+    words(Z(), Z(), A, B, H);
+    q6_quarter_run<NTOK, 0, 0>(A, B, H, scw, xslot, tl, th);
+    words(Z(), O(), A, B, H);
+    q6_quarter_run<NTOK, 0, 1>(A, B, H, scw, xslot, tl, th);
+    words(O(), Z(), A, B, H);
+    q6_quarter_run<NTOK, 1, 0>(A, B, H, scw, xslot, tl, th);
+    words(O(), O(), A, B, H);
+    q6_quarter_run<NTOK, 1, 1>(A, B, H, scw, xslot, tl, th);
+    const float d24 = d * kTwo24;
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + d24 * __builtin_fmaf(th[t], 0.0625f, tl[t]);
+}
+
 // acc[t] += the contribution of the Q6_K block whose aligned words start at
 // `row` (LDS), shifted by sh bits, with word 52 given apart; x at xslot.
 // The block's sum is formed from zero and then added, so that a block adds
@@ -490,22 +664,31 @@ __device__ __forceinline__ void q6_block_mac(const uint8_t* row, uint32_t w52, u
                                              float (&acc)[NTOK]) {
     // words 48..51 (scales) and word 52 (scales 14-15 and d, or d alone)
     const uint4 s4 = lds_read4(row + 4 * 48);
-    uint32_t scw[4];
-    scw[0] = __builtin_amdgcn_alignbit(s4.y, s4.x, sh);
-    scw[1] = __builtin_amdgcn_alignbit(s4.z, s4.y, sh);
-    scw[2] = __builtin_amdgcn_alignbit(s4.w, s4.z, sh);
-    scw[3] = __builtin_amdgcn_alignbit(w52, s4.w, sh);
-    const float d = f16_to_f32((w52 >> sh) & 0xFFFFu);
-    float tl[NTOK], th[NTOK];
+    q6_block<NTOK>(s4.x, s4.y, s4.z, s4.w, w52, sh, [&](auto n, auto kh, uint32_t (&A)[4], uint32_t (&B)[4],
+                                                        uint32_t (&H)[4]) {
+        constexpr int N = decltype(n)::value, KH = decltype(kh)::value;
+        q6_read4(row, 16 * N + 4 * KH, sh, A);
+        q6_read4(row, 16 * N + 8 + 4 * KH, sh, B);
+        q6_read4(row, 32 + 8 * N + 4 * KH, sh, H);
+    }, xslot, acc);
+}
+
+// The same from the block's 53 aligned words held in registers (wd[i] =
+// word i of the block's aligned span, shifted by sh bits).
+template <int NTOK>
+__device__ __forceinline__ void q6_block_mac_regs(const uint32_t (&wd)[53], uint32_t sh, const uint8_t* xslot,
+                                                  float (&acc)[NTOK]) {
+    q6_block<NTOK>(wd[48], wd[49], wd[50], wd[51], wd[52], sh, [&](auto n, auto kh, uint32_t (&A)[4],
+                                                                   uint32_t (&B)[4], uint32_t (&H)[4]) {
+        constexpr int N = decltype(n)::value, KH = decltype(kh)::value;
+        constexpr int ia = 16 * N + 4 * KH, ib = 16 * N + 8 + 4 * KH, ih = 32 + 8 * N + 4 * KH;
 #pragma unroll
-    for (int t = 0; t < NTOK; ++t) { tl[t] = 0.0f; th[t] = 0.0f; }
-    q6_quarter_run<NTOK, 0, 0>(row, sh, scw, xslot, tl, th);
-    q6_quarter_run<NTOK, 0, 1>(row, sh, scw, xslot, tl, th);
-    q6_quarter_run<NTOK, 1, 0>(row, sh, scw, xslot, tl, th);
-    q6_quarter_run<NTOK, 1, 1>(row, sh, scw, xslot, tl, th);
-    const float d24 = d * kTwo24;
-#pragma unroll
-    for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + d24 * __builtin_fmaf(th[t], 0.0625f, tl[t]);
+        for (int q = 0; q < 4; ++q) {
+            A[q] = __builtin_amdgcn_alignbit(wd[ia + q + 1], wd[ia + q], sh);
+            B[q] = __builtin_amdgcn_alignbit(wd[ib + q + 1], wd[ib + q], sh);
+            H[q] = __builtin_amdgcn_alignbit(wd[ih + q + 1], wd[ih + q], sh);
+        }
+    }, xslot, acc);
 }
 
 // Per-lane staging offsets of a 64-row Q6_K column.  Chunk q = 64*i + lane
@@ -522,7 +705,7 @@ struct Q6Offsets {
     uint32_t off52;
     uint32_t odd;
     __device__ __forceinline__ void init(const KqDesc& T) {
-        int lane = threadIdx.x;
+        int lane = kq_lane();
         asm volatile("" : "+v"(lane));
         const uint32_t rb = (uint32_t)T.row_bytes;
         uint32_t m = 0;
@@ -585,7 +768,7 @@ struct Q6Column {
         xs.load(T, valid ? b : 0);
     }
     __device__ __forceinline__ void commit(uint8_t* slot) const {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int i = 0; i < kQ6Chunks; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         reinterpret_cast<uint32_t*>(slot + kTileRows * kQ6LdsRow)[lane] = lane == tail_row ? tailv : w52;
@@ -593,7 +776,7 @@ struct Q6Column {
     }
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
                                                    float (&acc)[NTOK]) {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
         // the block starts 2 bytes into its first staged word when its index
         // in the tensor, (r0+lane)*nb + b, is odd
         const uint32_t sh = !ALT ? 16u * (uint32_t)(b & 1)
@@ -617,12 +800,12 @@ struct Q6Pair {
     static constexpr int CH = 26;                              // chunks of a row's pair
     static constexpr int ROWB = 16 * CH;                       // 416: odd multiple of 16
     static constexpr int N = TR * CH / 64;                     // loads a lane: 13
-    static constexpr int WSLOT = TR * ROWB + 4 * TR;
+    static constexpr int WSLOT = TR * ROWB + 4 * 64;           // word 104 of each lane's row, then x
     struct Offsets {
         uint32_t off[N];
         uint32_t off104;
         __device__ __forceinline__ void init(const KqDesc& T) {
-            int lane = threadIdx.x;
+            int lane = kq_lane();
             asm volatile("" : "+v"(lane));
             const uint32_t rb = (uint32_t)T.row_bytes;
 #pragma unroll
@@ -637,6 +820,47 @@ struct Q6Pair {
     uint4 stg[N];
     uint32_t w104;
     XStage<NTOK> xs0, xs1;
+    // ---- the pipelined kernel's pieces (as in K45Pair): word 104 of row
+    // (lane & 31) lands at word `lane` of its array (lanes 32..63 repeat
+    // rows 0..31); a lane's block is 53 aligned words, shifted 16 bits for
+    // the pair's second block
+    static constexpr int LOADS = N + 1 + 2 * NTOK;             // direct loads of one step
+    static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
+    static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
+        const int rows_here = min(TR, T.rows - tile * TR);
+        const uint32_t rb = (uint32_t)T.row_bytes;
+        const uint32_t max_off = (uint32_t)(rows_here - 1) * rb + 16u * (CH - 1);
+        const uint32_t max104 = (uint32_t)(rows_here - 1) * rb + 416u;
+        gbytes_t col = gbytes(T.w) + (size_t)tile * TR * T.row_bytes + (size_t)210 * b;
+#pragma unroll
+        for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
+        kq::dma<4>(col + min(o.off104, max104), wslot + TR * ROWB);
+    }
+    static __device__ __forceinline__ void dma_x(const KqDesc& T, int b, uint8_t* xslot) {
+        const int lane = kq_lane();
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) {
+            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane), xslot + 1024 * t);
+            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (b + 1) + 4 * lane), xslot + 1024 * (NTOK + t));
+        }
+    }
+    struct Regs {
+        uint32_t wd[53];
+    };
+    static __device__ __forceinline__ void load_regs(const uint8_t* wslot, Regs& r) {
+        const int lane = kq_lane(), k = lane & 1, rr = lane >> 1;
+        const uint8_t* rowp = wslot + rr * ROWB + k * 208;
+#pragma unroll
+        for (int i = 0; i < 13; ++i) {
+            const uint4 q = lds_read4(rowp + 16 * i);
+            r.wd[4 * i] = q.x; r.wd[4 * i + 1] = q.y; r.wd[4 * i + 2] = q.z; r.wd[4 * i + 3] = q.w;
+        }
+        r.wd[52] = k ? lds_read1(wslot + TR * ROWB + 4 * rr) : lds_read1(rowp + 208);
+    }
+    static __device__ __forceinline__ void compute_regs(const Regs& r, const uint8_t* xslot, float (&acc)[NTOK]) {
+        const int k = kq_lane() & 1;
+        q6_block_mac_regs<NTOK>(r.wd, k ? 16u : 0u, xslot + k * 1024 * NTOK, acc);
+    }
 
     __device__ __forceinline__ void stage(const KqDesc& T, const Offsets& o, int tile, int b, bool valid) {
         const int rows_here = min(TR, T.rows - tile * TR);
@@ -652,7 +876,7 @@ struct Q6Pair {
         xs1.load(T, valid ? b + 1 : 1);
     }
     __device__ __forceinline__ void commit(uint8_t* slot) const {
-        const int lane = threadIdx.x;
+        const int lane = kq_lane();
 #pragma unroll
         for (int i = 0; i < N; ++i) reinterpret_cast<uint4*>(slot)[64 * i + lane] = stg[i];
         reinterpret_cast<uint32_t*>(slot + TR * ROWB)[lane & 31] = w104;     // lanes 32..63 repeat 0..31
@@ -662,7 +886,7 @@ struct Q6Pair {
     static __device__ __forceinline__ void compute(const KqDesc& T, const uint8_t* slot, int tile, int b,
                                                    float (&acc)[NTOK]) {
         (void)T; (void)tile; (void)b;
-        const int lane = threadIdx.x, k = lane & 1, r = lane >> 1;
+        const int lane = kq_lane(), k = lane & 1, r = lane >> 1;
         const uint8_t* rowp = slot + r * ROWB + k * 208;
         const uint32_t w52 = k ? lds_read1(slot + TR * ROWB + 4 * r) : lds_read1(rowp + 208);
         q6_block_mac<NTOK>(rowp, w52, k ? 16u : 0u, slot + WSLOT + k * 1024 * NTOK, acc);
@@ -674,7 +898,7 @@ struct Q6Pair {
 // the even lane of the pair that holds the row.
 template <int NTOK, int TR>
 __device__ __forceinline__ void write_rows(const KqDesc& T, int tile, const float (&v)[NTOK]) {
-    const int lane = threadIdx.x;
+    const int lane = kq_lane();
     const int r = TR == kTileRows ? lane : lane >> 1;
     const int r0 = tile * TR;
     if ((TR == kTileRows || (lane & 1) == 0) && r < T.rows - r0) {
@@ -705,7 +929,7 @@ __device__ __forceinline__ int shared_slot(const KqDesc& T, int tile) {
 // device-coherence bit), so no L2-wide writeback/invalidate is needed.
 template <int NTOK>
 __device__ __forceinline__ void store_partial(const KqDesc& T, int slot, int seg, const float (&v)[NTOK]) {
-    const int lane = threadIdx.x;
+    const int lane = kq_lane();
     gfloat_t dst = gfloat(T.partials) + ((size_t)slot * T.nseg + seg) * (NTOK * kTileRows);
 #pragma unroll
     for (int t = 0; t < NTOK; ++t)
@@ -719,7 +943,7 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, int slot, int seg
 // counter for the next launch.
 template <int NTOK, int TR>
 __device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int count) {
-    const int lane = threadIdx.x;
+    const int lane = kq_lane();
     __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
     uint32_t old = 0;
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -947,6 +1171,250 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
         if (T.nb & 1) run_segments<Q6Column<NTOK, true>, NTOK, kDepthQ6<NTOK>>(T, j0, j1, slot);
         else run_segments<Q6Column<NTOK, false>, NTOK, kDepthQ6<NTOK>>(T, j0, j1, slot);
         break;
+    }
+}
+
+// ------------------------------------------------------------ the pipelined kernel
+// Launches whose tensors all run in 32-row tiles with two-block segments
+// (every decode set and every large matrix at one token plane, at two up to
+// 16384 rows) take this kernel: one workgroup a compute unit, holding two
+// kinds of waves.
+//   * Producers (kPcProducers) only move bytes.  A producer issues the direct
+//     global -> LDS loads of its steps into a ring of LDS slots, keeps several
+//     steps in flight, waits for the oldest with vmcnt and publishes its slot.
+//   * Consumers (kPcConsumers) only compute.  Consumer c takes positions c,
+//     c + kPcConsumers, ... of the workgroup's run, waits for the slot,
+//     computes the step exactly as kq_matvec_kernel does, and frees it.
+// So no wave waits to issue a load while it holds data to compute, and the
+// run's bytes are requested as fast as the ring frees.  Position n of the
+// run is segment j0 + n (one step: 32 rows x 2 blocks) in slot n % R.  The
+// pair-added segment sum goes to its tile: a tile whose segments all lie in
+// the run is folded in LDS, in segment order, by the consumer whose delivery
+// completes it; a tile shared with other workgroups goes through the
+// workspace exactly as in kq_matvec_kernel, so the bits are those of
+// kq_matvec_kernel for the same plan.
+// Deadlock freedom: a consumer frees its slot before delivering, and waits
+// only for the tile-fold slot it delivers to (until the tile TS places
+// earlier is folded), so the lowest undelivered position can always go on.
+// Every wait is bounded: a broken handshake ends the wave (wrong results),
+// it never hangs the GPU.
+constexpr int kPcProducers = 2, kPcConsumers = 8, kPcWaves = kPcProducers + kPcConsumers;
+constexpr int kPcSpin = 1 << 22;
+
+// s_waitcnt for vmcnt <= N (expcnt and lgkmcnt not waited for)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited for)
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
+typedef __attribute__((address_space(3))) volatile uint32_t* lsync_t;
+
+// Waits until *f == v, at most kPcSpin polls; false on time-out.
+__device__ __forceinline__ bool spin_until(lsync_t f, uint32_t v) {
+    for (int k = 0; k < kPcSpin; ++k) {
+        if (*f == v) return true;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return false;
+}
+
+// The LDS of one workgroup for tensor T.  Dynamic (offsets in bytes): R
+// weight slots of W bytes, RX x slots of X bytes, then the fold slots'
+// segment sums [TS][nseg][NTOK][32] floats.  Static (kq_pc_sync, words):
+// ready[R] (position + 1 once its weights and x are in), wdone[R] (position +
+// 1 once its weights are read into registers), xdone[RX] (once its x is no
+// longer read), owner[TS] and count[TS] of the fold slots.  The flags live
+// in an array of their own, apart from the slots the direct loads write, so
+// polling them needs no wait for the loads in flight.
+constexpr int kPcMaxSlots = 16, kPcMaxFold = 8;
+struct PcLayout {
+    int R, RX, TS, W, X, xs, sums;
+    __device__ __forceinline__ PcLayout(const KqDesc& T, int w, int x) {
+        R = T.reserved0 & 255;
+        TS = (T.reserved0 >> 8) & 255;
+        RX = (T.reserved0 >> 16) & 255;
+        W = w;
+        X = x;
+        xs = R * W;
+        sums = xs + RX * X;
+    }
+    static constexpr int ready = 0, wdone = kPcMaxSlots, xdone = 2 * kPcMaxSlots, owner = 3 * kPcMaxSlots,
+                         count = 3 * kPcMaxSlots + kPcMaxFold, words = 3 * kPcMaxSlots + 2 * kPcMaxFold;
+};
+
+// The steps of one producer: positions p, p + kPcProducers, ... of the run.
+// Before issuing position n it waits until position n - R has left its
+// weight slot and n - RX its x slot (R and RX are multiples of
+// kPcProducers of at least kPcProducers * D, so those positions are its own
+// and already published).
+template <class Col, int NTOK>
+__device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, uint8_t* lds, lsync_t sync,
+                                           const PcLayout& Y, int p) {
+    constexpr int D = 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4;     // steps in flight: D * LOADS <= 63
+    static_assert(D >= 2, "two steps in flight");
+    typename Col::Offsets offs;
+    offs.init(T);
+    const int nseg = T.nseg;
+    int issued = 0, published = 0;
+    for (int n = p; n < nsteps; n += kPcProducers) {
+        const int ws = n % Y.R, xs = n % Y.RX;
+        if (n >= Y.R && !spin_until(sync + PcLayout::wdone + ws, (uint32_t)(n - Y.R + 1))) return;
+        if (n >= Y.RX && !spin_until(sync + PcLayout::xdone + xs, (uint32_t)(n - Y.RX + 1))) return;
+        const int j = j0 + n, tile = j / nseg, b = 2 * (j - tile * nseg);
+        Col::dma_w(T, offs, tile, b, lds + ws * Y.W);
+        Col::dma_x(T, b, lds + Y.xs + xs * Y.X);
+        ++issued;
+        if (issued - published == D) {
+            wait_vm<(D - 1) * Col::LOADS>();
+            const int pos = p + kPcProducers * published;
+            if (kq_lane() == 0) sync[PcLayout::ready + pos % Y.R] = (uint32_t)(pos + 1);
+            ++published;
+        }
+    }
+    while (published < issued) {
+        const int left = issued - published - 1;       // steps that may stay in flight
+        if (left >= 3) wait_vm<3 * Col::LOADS>();
+        else if (left == 2) wait_vm<2 * Col::LOADS>();
+        else if (left == 1) wait_vm<Col::LOADS>();
+        else wait_vm<0>();
+        const int pos = p + kPcProducers * published;
+        if (kq_lane() == 0) sync[PcLayout::ready + pos % Y.R] = (uint32_t)(pos + 1);
+        ++published;
+    }
+}
+
+// The steps of one consumer: positions c, c + kPcConsumers, ... of the run.
+template <class Col, int NTOK>
+__device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint8_t* lds, lsync_t sync,
+                                           const PcLayout& Y, int c) {
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    const int lane = kq_lane();
+    const int nseg = T.nseg, nsteps = j1 - j0;
+    const int first_owned = (j0 + nseg - 1) / nseg;     // first tile that lies wholly in the run
+    for (int n = c; n < nsteps; n += kPcConsumers) {
+        const int ws = n % Y.R, xs = n % Y.RX;
+        if (!spin_until(sync + PcLayout::ready + ws, (uint32_t)(n + 1))) return;
+        const int j = j0 + n, tile = j / nseg, seg = j - tile * nseg;
+        typename Col::Regs regs;
+        Col::load_regs(lds + ws * Y.W, regs);
+        wait_lds();                                      // the block is in registers
+        if (lane == 0) sync[PcLayout::wdone + ws] = (uint32_t)(n + 1);
+        late_priority(t_start);
+        float acc[NTOK];
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
+        Col::compute_regs(regs, lds + Y.xs + xs * Y.X, acc);
+        wait_lds();                                      // every read of the x slot is done
+        if (lane == 0) sync[PcLayout::xdone + xs] = (uint32_t)(n + 1);
+#pragma unroll
+        for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + dpp_xor1(acc[t]);     // the pair's two blocks
+        if (tile * nseg >= j0 && (tile + 1) * nseg <= j1) {
+            // a tile of this run: fold slot (tile - first_owned) % TS, free once
+            // the tile TS places earlier has been folded
+            const int ts = (tile - first_owned) % Y.TS;
+            if (!spin_until(sync + PcLayout::owner + ts, (uint32_t)tile)) return;
+            uint8_t* sums = lds + Y.sums + ((ts * nseg + seg) * NTOK) * 128;     // [TS][nseg][NTOK][32] floats
+            if ((lane & 1) == 0) {
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) reinterpret_cast<float*>(sums)[32 * t + (lane >> 1)] = acc[t];
+            }
+            wait_lds();
+            uint32_t old = 0;
+            if (lane == 0)
+                old = __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(sync + PcLayout::count + ts), 1u,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            old = __builtin_amdgcn_readfirstlane(old);
+            if (old == (uint32_t)(nseg - 1)) {
+                float sum[NTOK];
+#pragma unroll
+                for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
+                for (int s2 = 0; s2 < nseg; ++s2) {
+                    const float* ss = reinterpret_cast<const float*>(lds + Y.sums + ((ts * nseg + s2) * NTOK) * 128);
+#pragma unroll
+                    for (int t = 0; t < NTOK; ++t) sum[t] = sum[t] + ss[32 * t + (lane >> 1)];
+                }
+                write_rows<NTOK, 32>(T, tile, sum);
+                wait_lds();
+                if (lane == 0) {
+                    sync[PcLayout::count + ts] = 0u;
+                    sync[PcLayout::owner + ts] = (uint32_t)(tile + Y.TS);
+                }
+            }
+        } else {
+            const int wslot = shared_slot(T, tile);
+            store_partial<NTOK>(T, wslot, seg, acc);
+            arrive<NTOK, 32>(T, tile, wslot, 1);
+        }
+    }
+}
+
+template <class Col, int NTOK>
+__device__ __forceinline__ void pc_run(const KqDesc& T, int j0, int j1, uint8_t* lds, lsync_t sync, int wave) {
+    const PcLayout Y(T, Col::PC_W, Col::PC_X);
+    // flags zero, fold slots owned by the run's first TS whole tiles
+    const int first_owned = (j0 + T.nseg - 1) / T.nseg;
+    for (int k = threadIdx.x; k < 3 * kPcMaxSlots; k += blockDim.x) sync[k] = 0u;
+    for (int k = threadIdx.x; k < kPcMaxFold; k += blockDim.x) {
+        sync[PcLayout::owner + k] = (uint32_t)(first_owned + k);
+        sync[PcLayout::count + k] = 0u;
+    }
+    __syncthreads();
+    if (wave < kPcProducers) {
+        __builtin_amdgcn_s_setprio(3);
+        pc_produce<Col, NTOK>(T, j0, j1 - j0, lds, sync, Y, wave);
+    } else {
+        pc_consume<Col, NTOK>(T, j0, j1, lds, sync, Y, wave - kPcProducers);
+    }
+}
+
+template <int NTOK>
+__global__ __launch_bounds__(64 * kPcWaves, 1) void kq_pc_kernel(const KqLaunch L) {
+    extern __shared__ uint4 kq_pc_lds[];
+    __shared__ uint32_t kq_pc_sync[PcLayout::words];
+    uint8_t* lds = reinterpret_cast<uint8_t*>(kq_pc_lds);
+    const lsync_t sync = (lsync_t)(kq_pc_sync);
+    const int w = xcd_remap(blockIdx.x, gridDim.x);
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));    // uniform: scalar bookkeeping
+    const u32x8* hp = reinterpret_cast<const u32x8*>(&L.h);
+    const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2];
+    asm volatile("" : : "s"(g0), "s"(g1), "s"(g2));
+    const int n = (int)g0[0];
+    int i = 0;
+#pragma unroll
+    for (int k = 0; k < kMaxSet; ++k) i += (int)(k < 8 ? g1[k] : g2[k - 8]) <= w ? 1 : 0;
+    if (i >= n) return;
+    const KqDesc T = load_uniform(L.t[i]);
+    const int u = w - T.wg_base;
+    const int j0 = u * T.seg_q + min(u, T.seg_r);
+    const int j1 = j0 + T.seg_q + (u < T.seg_r ? 1 : 0);
+    switch (T.fmt) {
+    case KQ_Q4_K: pc_run<K45Pair<KQ_Q4_K, NTOK>, NTOK>(T, j0, j1, lds, sync, wave); break;
+    case KQ_Q5_K: pc_run<K45Pair<KQ_Q5_K, NTOK>, NTOK>(T, j0, j1, lds, sync, wave); break;
+    default: pc_run<Q6Pair<NTOK>, NTOK>(T, j0, j1, lds, sync, wave); break;
+    }
+}
+
+// The pipelined kernel's sizes for a tensor of this format at ntok (1 or
+// 2): LDS bytes of a step's weights (*w) and x (*x), and D, the steps a
+// producer keeps in flight.
+template <class Col>
+static void pc_sizes_t(int* w, int* x, int* d) {
+    *w = Col::PC_W;
+    *x = Col::PC_X;
+    *d = 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4;
+}
+void pc_sizes(int32_t fmt, int32_t ntok, int* w, int* x, int* d) {
+    if (ntok == 1) {
+        if (fmt == KQ_Q4_K) pc_sizes_t<K45Pair<KQ_Q4_K, 1>>(w, x, d);
+        else if (fmt == KQ_Q5_K) pc_sizes_t<K45Pair<KQ_Q5_K, 1>>(w, x, d);
+        else pc_sizes_t<Q6Pair<1>>(w, x, d);
+    } else {
+        if (fmt == KQ_Q4_K) pc_sizes_t<K45Pair<KQ_Q4_K, 2>>(w, x, d);
+        else if (fmt == KQ_Q5_K) pc_sizes_t<K45Pair<KQ_Q5_K, 2>>(w, x, d);
+        else pc_sizes_t<Q6Pair<2>>(w, x, d);
     }
 }
 
@@ -1604,10 +2072,68 @@ static int capacity_t(int lds_bytes) {
     return min(resident_per_cu<NTOK>(lds_bytes), kMaxWavesPerCU) * cus;
 }
 
-// One round of resident one-wave workgroups of kq_matvec_kernel<ntok> with
-// this LDS size on the current device (at most two waves a SIMD).
-int launch_capacity(int32_t ntok, int32_t lds_bytes) {
-    switch (ntok) {
+// Whether launches may take the pipelined kernel: on unless the
+// environment sets KQMV_PIPELINE=0, or kq_debug_set_pipeline switched it.
+static int g_pipeline = -1;
+void set_pipeline(int on) { g_pipeline = on ? 1 : 0; }
+static bool pipeline_enabled() {
+    if (g_pipeline < 0) {
+        const char* e = getenv("KQMV_PIPELINE");
+        g_pipeline = (e && e[0] == '0') ? 0 : 1;
+    }
+    return g_pipeline == 1;
+}
+
+// Sets L up for the pipelined kernel when every tensor runs in 32-row tiles
+// at ntok <= 2 and each tensor's ring of at least 8 step slots, with its 3
+// fold slots, fits one workgroup's LDS: each descriptor gets its ring slots R
+// (even, at most 16) and fold slots TS, the launch its LDS size.  Returns
+// whether it did (L->pipelined).
+int plan_pipelined(KqLaunch* L) {
+    L->pipelined = 0;
+    if (!pipeline_enabled() || L->ntok > 2) return 0;
+    static int lds_max[16] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    int& lm = lds_max[dev & 15];
+    if (lm == 0 && (hipDeviceGetAttribute(&lm, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || lm <= 0))
+        lm = -1;
+    if (lm < 0) return 0;
+    const int budget = lm - (int)sizeof(uint32_t) * PcLayout::words - 64;
+    constexpr int TS = 3;
+    int lds = 0;
+    for (int i = 0; i < L->h.n; ++i) {
+        if (L->t[i].tile_rows != 32) return 0;
+    }
+    for (int i = 0; i < L->h.n; ++i) {
+        KqDesc& D = L->t[i];
+        int wb = 0, xb = 0, d = 0;
+        pc_sizes(D.fmt, L->ntok, &wb, &xb, &d);
+        // x slots: twice the steps both producers keep in flight (held while
+        // a step computes); weight slots: as many as the rest of the LDS
+        // holds (freed as soon as a consumer has its block in registers)
+        const int RX = 4 * d;
+        const int sums = TS * D.nseg * L->ntok * 128;
+        int R = (budget - sums - RX * xb) / wb;
+        R = (R > kPcMaxSlots ? kPcMaxSlots : R) & ~1;
+        if (R < 2 * d || RX > kPcMaxSlots) return 0;
+        D.reserved0 = R | (TS << 8) | (RX << 16);
+        const int need = R * wb + RX * xb + sums;
+        if (need > lds) lds = need;
+    }
+    L->lds_bytes = lds;
+    L->pipelined = 1;
+    return 1;
+}
+
+// One round of resident workgroups for L on the current device: one
+// workgroup a compute unit for the pipelined kernel, else one-wave
+// workgroups of kq_matvec_kernel<ntok> with L's LDS size (at most two waves
+// a SIMD).
+int launch_capacity(const KqLaunch& L) {
+    if (L.pipelined) return compute_units();
+    const int32_t lds_bytes = L.lds_bytes;
+    switch (L.ntok) {
     case 1: return capacity_t<1>(lds_bytes);
     case 2: return capacity_t<2>(lds_bytes);
     case 3: return capacity_t<3>(lds_bytes);
@@ -1623,6 +2149,12 @@ int launch_capacity(int32_t ntok, int32_t lds_bytes) {
 int launch_matvec(const KqLaunch& L, hipStream_t stream) {
     const dim3 grid((unsigned)L.grid), block(64);
     const size_t lds = (size_t)L.lds_bytes;
+    if (L.pipelined) {
+        const dim3 pblock(64 * kPcWaves);
+        if (L.ntok == 1) hipLaunchKernelGGL(kq_pc_kernel<1>, grid, pblock, lds, stream, L);
+        else hipLaunchKernelGGL(kq_pc_kernel<2>, grid, pblock, lds, stream, L);
+        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
+    }
     switch (L.ntok) {
     case 1: hipLaunchKernelGGL(kq_matvec_kernel<1>, grid, block, lds, stream, L); break;
     case 2: hipLaunchKernelGGL(kq_matvec_kernel<2>, grid, block, lds, stream, L); break;

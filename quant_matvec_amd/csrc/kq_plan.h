@@ -44,8 +44,9 @@ constexpr int kSlotBytesQ5K = kTileRows * 176;
 constexpr int kSlotBytesQ6K = kTileRows * 208 + 4 * kTileRows;
 // 32-row tiles stage the two blocks of a segment per step: Q4_K/Q5_K the
 // same bytes as a 64-row column; Q6_K 32 rows of 26 chunks (words 0..103
-// of the pair's 105) and word 104 of each row apart.
-constexpr int kSlotBytesQ6KPair = 32 * 416 + 4 * 32;
+// of the pair's 105) and word 104 of each row apart (64 words: the direct
+// loads of the pipelined kernel write one per lane).
+constexpr int kSlotBytesQ6KPair = 32 * 416 + 4 * 64;
 
 struct KqDesc {
     const uint8_t* w;
@@ -68,7 +69,7 @@ struct KqDesc {
     float* partials;    // this tensor's shared-tile slots in the workspace: [P-1][nseg][ntok][64]
     uint32_t* counters; // this tensor's arrival counters: one per slot, zero between calls
     int32_t tile_rows;  // 64, or 32 for a large matrix (two lanes a row, a segment a step)
-    int32_t reserved0;
+    int32_t reserved0;  // pipelined kernel: weight slots R | fold slots TS << 8 | x slots RX << 16
     int64_t reserved1;
 };
 static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
@@ -90,6 +91,8 @@ struct KqLaunch {
     int32_t grid;         // workgroups
     int32_t lds_bytes;
     int32_t total_segments;
+    int32_t pipelined;    // run by the producer/consumer kernel (one workgroup a compute unit)
+    int32_t reserved;
 };
 
 struct KqPlanSizes {

@@ -106,10 +106,10 @@ def test_cancelling_rows_in_a_set(fmt, frac):
 
 # (rows, cols) -> groups of ntok that share one plan for every format
 NTOK_SHAPES = {
-    (131, 6656): [list(range(1, 9))],          # 64-row tiles, one-block segments
+    (131, 6656): [[1, 2], list(range(3, 9))],  # 32-row two-block at ntok 1-2; 64-row one-block at 3-8
     (1100, 2304): [list(range(1, 9))],         # odd blocks a row: 64-row tiles, two-block (Q6_K one-block)
     (1100, 2560): [list(range(1, 9))],         # 32-row tiles at ntok 1-2, 64-row at 3-8, two-block segments
-    (1100, 6656): [[1, 2], list(range(3, 9))],  # 32-row four-block at ntok 1-2; 64-row two-block at 3-8
+    (1100, 6656): [list(range(1, 9))],         # 32-row tiles at ntok 1-2, 64-row at 3-8, two-block segments
 }
 
 
@@ -267,3 +267,56 @@ def test_stream52_all_layers_all_rows():
         for T in tensors:
             y_ref, s = oracle.matvec(T.fmt, ws[T.name], T.rows, T.cols, xs[T.xkey], nthreads=NTHREADS)
             check_tol(host(ys[T.name]), y_ref, s, "stream layer %d %s" % (li, T.name))
+
+
+# ---- the pipelined producer/consumer kernel against the one-wave kernel:
+# launches whose tensors all run in 32-row tiles at ntok <= 2 take the
+# pipelined kernel; forbidding it makes the same launch run in the one-wave
+# kernel, and both must give the same bits (same plan, same sums in the same
+# order).
+
+PIPE_CASES = [
+    ("qkvg set", [(Q4_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0), (Q6_K, 256, 6656, 0), (Q4_K, 4096, 6656, 0)], 1),
+    ("q5 set ntok2", [(Q5_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0)], 2),
+    ("kv pair small", [(Q6_K, 256, 6656, 0), (Q5_K, 256, 6656, 1)], 1),
+    ("ragged large", [(Q6_K, 20037, 6656, 0)], 1),
+    ("short rows", [(Q4_K, 3000, 512, 0), (Q5_K, 77, 1024, 1), (Q6_K, 1, 256, 2)], 2),
+    ("long rows", [(Q4_K, 2050, 19968, 0)], 1),
+    ("mixed plans", [(Q4_K, 4096, 6656, 0), (Q6_K, 300, 2304, 1)], 1),     # odd blocks: one-wave kernel
+]
+
+
+@pytest.mark.parametrize("name,specs,ntok", PIPE_CASES, ids=[c[0] for c in PIPE_CASES])
+def test_pipelined_kernel_bitwise_equals_one_wave_kernel(name, specs, ntok):
+    t = torch()
+    xcols = {}
+    for f, r, c, xi in specs:
+        xcols[xi] = max(c, xcols.get(xi, 0))
+    xs = {xi: kqgen.activations(ntok, c, 680, xi, ntok) for xi, c in xcols.items()}
+    dxs = {xi: dev(v) for xi, v in xs.items()}
+    ws = [kqgen.weights(f, r, c, 681, i, r) for i, (f, r, c, _) in enumerate(specs)]
+    dws = [dev(w.reshape(-1)) for w in ws]
+    outs = {}
+    for pipe in (True, False):
+        kq.kq_debug_set_pipeline(pipe)
+        try:
+            ys = [t.full((ntok, r), float("nan"), dtype=t.float32, device="cuda") for (_, r, _, _) in specs]
+            note("pipelined vs one-wave: %s ntok=%d pipeline=%s" % (name, ntok, pipe))
+            members = kq.make_set([dict(fmt=f, w=dw, x=dxs[xi], y=y, rows=r, cols=c, ldx=xcols[xi])
+                                   for (f, r, c, xi), dw, y in zip(specs, dws, ys)])
+            kernel = kq.kq_debug_plan_kernel(members, ntok=ntok)
+            if not pipe or name == "mixed plans":
+                assert kernel == "kq_matvec_kernel<%d>" % ntok, kernel
+            elif name in ("qkvg set", "q5 set ntok2", "ragged large", "long rows"):
+                assert kernel == "kq_pc_kernel<%d>" % ntok, kernel
+            kq.kq_matvec_set(members, ntok=ntok)
+            outs[pipe] = [host(y) for y in ys]
+        finally:
+            kq.kq_debug_set_pipeline(True)
+    for i, ((f, r, c, xi), w) in enumerate(zip(specs, ws)):
+        assert np.array_equal(_bits(outs[True][i]), _bits(outs[False][i])), i
+        x = np.ascontiguousarray(xs[xi][:, :c])
+        idx = np.unique(np.concatenate([np.arange(min(r, 70)), np.arange(max(0, r - 70), r),
+                                        np.random.default_rng(682).integers(0, r, 300)]))
+        y_ref, s = oracle.matvec(f, w, r, c, x, row_idx=idx, nthreads=NTHREADS)
+        check_tol(outs[True][i][:, idx], y_ref, s, "%s member %d" % (name, i))

@@ -105,9 +105,13 @@ def test_matvec_ntok(fmt, ntok):
     y = gpu_matvec(fmt, w, rows, cols, x, ldx=cols + 4, ldy=rows + 3)
     y_ref, s = oracle.matvec(fmt, w, rows, cols, x)
     check_tol(y, y_ref, s, "fmt %d ntok %d" % (fmt, ntok))
-    # every column of an ntok call is bitwise the ntok=1 result on that column
+    # every column is bitwise the call with fewer planes of the same plan on
+    # it: ntok 1 and 2 share 32-row tiles of two-block segments, ntok 3 and
+    # more 64-row tiles of one-block segments (at most 1024 rows)
+    ref = 1 if ntok <= 2 else 3
     for t in range(ntok):
-        y1 = gpu_matvec(fmt, w, rows, cols, x[t:t + 1])
+        xr = np.repeat(x[t:t + 1], ref, axis=0)
+        y1 = gpu_matvec(fmt, w, rows, cols, xr)
         assert np.array_equal(y1[0].view(np.uint32), y[t].view(np.uint32)), t
 
 
@@ -325,10 +329,10 @@ def test_mid_matrix_ntok_columns_bitwise(fmt, ntok):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_long_row_plans_across_ntok(fmt):
-    """Rows of 26 blocks in 32-row tiles (ntok 1 and 2) take four-block
-    segments, in 64-row tiles (ntok 3 and more) two-block ones: planes
-    match bitwise between calls of the same plan, and every call meets the
-    tolerance."""
+    """Rows of 26 blocks run in 32-row tiles at ntok 1 and 2 and in 64-row
+    tiles at ntok 3 and more, with two-block segments in both: planes match
+    bitwise between calls of the same plan (and across the two heights),
+    and every call meets the tolerance."""
     rows, cols = 4100, 6656
     w = kqgen.weights(fmt, rows, cols, 627, fmt)
     x = kqgen.activations(8, cols, 628, fmt)
