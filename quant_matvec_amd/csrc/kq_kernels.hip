@@ -855,7 +855,7 @@ struct Q6Pair {
             const uint4 q = lds_read4(rowp + 16 * i);
             r.wd[4 * i] = q.x; r.wd[4 * i + 1] = q.y; r.wd[4 * i + 2] = q.z; r.wd[4 * i + 3] = q.w;
         }
-        r.wd[52] = k ? lds_read1(wslot + TR * ROWB + 4 * rr) : lds_read1(rowp + 208);
+        r.wd[52] = lds_read1(k ? wslot + TR * ROWB + 4 * rr : rowp + 208);
     }
     static __device__ __forceinline__ void compute_regs(const Regs& r, const uint8_t* xslot, float (&acc)[NTOK]) {
         const int k = kq_lane() & 1;
@@ -936,25 +936,11 @@ __device__ __forceinline__ void store_partial(const KqDesc& T, int slot, int seg
         __hip_atomic_store(dst + t * kTileRows + lane, v[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// This workgroup stored `count` segment sums of a shared tile.  Ordering:
-// the stores are complete (vmcnt drained) before the counter moves, and
-// the last contributor reads the partials only after its increment
-// returned; it adds all segment sums of the tile in order and resets the
-// counter for the next launch.
-template <int NTOK, int TR>
-__device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int count) {
-    const int lane = kq_lane();
-    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
-    uint32_t old = 0;
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (lane == 0) old = __hip_atomic_fetch_add(ctr, (uint32_t)count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (old + (uint32_t)count != (uint32_t)T.nseg) return;
-    gfloat_t src = gfloat(T.partials) + (size_t)slot * T.nseg * (NTOK * kTileRows) + lane;
-    float sum[NTOK];
+// The segment sums of shared-tile slot `slot`, added in segment order
+// (sum[t] starts at zero), for this lane's row of a 64-lane slot.
+template <int NTOK>
+__device__ __forceinline__ void sum_partials(const KqDesc& T, int slot, float (&sum)[NTOK]) {
+    gfloat_t src = gfloat(T.partials) + (size_t)slot * T.nseg * (NTOK * kTileRows) + kq_lane();
 #pragma unroll
     for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
     // Batches of kFixBatch segment sums are requested together (indices past
@@ -979,8 +965,90 @@ __device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int 
             }
         }
     }
+}
+
+// This workgroup stored `count` segment sums of a shared tile.  Ordering:
+// the stores are complete (vmcnt drained) before the counter moves, and
+// the last contributor reads the partials only after its increment
+// returned; it adds all segment sums of the tile in order and resets the
+// counter for the next launch.
+template <int NTOK, int TR>
+__device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int count) {
+    const int lane = kq_lane();
+    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
+    uint32_t old = 0;
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (lane == 0) old = __hip_atomic_fetch_add(ctr, (uint32_t)count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (old + (uint32_t)count != (uint32_t)T.nseg) return;
+    float sum[NTOK];
+    sum_partials<NTOK>(T, slot, sum);
     write_rows<NTOK, TR>(T, tile, sum);
     if (lane == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- branch-free forms for the pipelined kernel.  Its loops must stay
+// uniform: a lane-conditional block (if (lane == 0) ...) ahead of a loop's
+// back edge lets the compiler split the loop so that lanes run different
+// iterations, and a value shared through readfirstlane then comes from the
+// wrong lane.  So every lane executes the same instructions: a flag store
+// or a counter update that belongs to lane 0 is made by every lane, lane 0
+// on the flag and lane i on a sink word of its own (no two lanes on one
+// word, so no serialization); global stores and atomics that only some
+// lanes may make go through buffer instructions whose out-of-range offset
+// makes the hardware drop the other lanes.
+constexpr uint32_t kBufDrop = 0x80000000u;      // a buffer offset past every range used here
+constexpr int kBufFlags = 0x00020000;           // raw 32-bit buffer resource, no format conversion
+typedef __attribute__((address_space(3))) volatile uint32_t* lsync_t;
+typedef __attribute__((address_space(3))) uint32_t* lword_t;
+
+// Lane 0's word w, the other lanes' sink words (sink[1..63]).
+__device__ __forceinline__ lsync_t lane0_word(lsync_t w, lsync_t sink) {
+    const int lane = kq_lane();
+    return lane == 0 ? w : sink + lane;
+}
+// *w = v (lane 0), sink words for the rest.
+__device__ __forceinline__ void lds_set(lsync_t w, lsync_t sink, uint32_t v) { *lane0_word(w, sink) = v; }
+// Old value of an LDS counter that this wave moves by one (uniform).
+__device__ __forceinline__ uint32_t lds_bump(lsync_t w, lsync_t sink) {
+    const uint32_t old = __hip_atomic_fetch_add((lword_t)lane0_word(w, sink), kq_lane() == 0 ? 1u : 0u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __builtin_amdgcn_readfirstlane(old);
+}
+
+// write_rows for a 32-row tile: the even lane of each pair stores its row.
+template <int NTOK>
+__device__ __forceinline__ void write_rows_bf(const KqDesc& T, int tile, const float (&v)[NTOK]) {
+    const int lane = kq_lane();
+    const int r0 = tile * 32, rows_here = min(32, T.rows - r0), r = lane >> 1;
+    const uint32_t off = ((lane & 1) == 0 && r < rows_here) ? 4u * (uint32_t)r : kBufDrop;
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+        const __amdgpu_buffer_rsrc_t y = __builtin_amdgcn_make_buffer_rsrc(T.y + t * T.ldy + r0, (short)0,
+                                                                          4 * rows_here, kBufFlags);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[t]), y, off, 0, 0);
+    }
+}
+
+// arrive(T, tile, slot, 1) for a 32-row tile, branch-free.
+template <int NTOK>
+__device__ __forceinline__ void arrive_bf(const KqDesc& T, int tile, int slot) {
+    __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    const __amdgpu_buffer_rsrc_t c = __builtin_amdgcn_make_buffer_rsrc(T.counters + slot, (short)0, 4, kBufFlags);
+    uint32_t old = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, c, kq_lane() == 0 ? 0u : kBufDrop, 0, 0);
+    old = __builtin_amdgcn_readfirstlane(old);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    if (old + 1u != (uint32_t)T.nseg) return;
+    float sum[NTOK];
+    sum_partials<NTOK>(T, slot, sum);
+    write_rows_bf<NTOK>(T, tile, sum);
+    __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);     // every lane: the same word
 }
 
 // A wave whose column arrives late gets the SIMD first: on a launch that
@@ -1182,9 +1250,16 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 //   * Producers (kPcProducers) only move bytes.  A producer issues the direct
 //     global -> LDS loads of its steps into a ring of LDS slots, keeps several
 //     steps in flight, waits for the oldest with vmcnt and publishes its slot.
-//   * Consumers (kPcConsumers) only compute.  Consumer c takes positions c,
-//     c + kPcConsumers, ... of the workgroup's run, waits for the slot,
-//     computes the step exactly as kq_matvec_kernel does, and frees it.
+//   * Consumers (pc_consumers(NTOK): 12 at one token plane, whose registers
+//     allow four waves a SIMD, else 8) only compute.  A free consumer claims the
+//     next position of the workgroup's run (an LDS counter), waits for its
+//     slot, copies its lane's block into registers, frees the slot and
+//     computes the step exactly as kq_matvec_kernel does.  Claiming in
+//     order, rather than a fixed share per consumer, frees each slot as soon
+//     as any consumer is idle.
+// x is either resident (every x block the run reads, loaded once at the
+// start, when it fits beside the weight ring) or streamed with each step
+// into a ring of its own, held until the step's products are done.
 // So no wave waits to issue a load while it holds data to compute, and the
 // run's bytes are requested as fast as the ring frees.  Position n of the
 // run is segment j0 + n (one step: 32 rows x 2 blocks) in slot n % R.  The
@@ -1193,12 +1268,15 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // completes it; a tile shared with other workgroups goes through the
 // workspace exactly as in kq_matvec_kernel, so the bits are those of
 // kq_matvec_kernel for the same plan.
-// Deadlock freedom: a consumer frees its slot before delivering, and waits
-// only for the tile-fold slot it delivers to (until the tile TS places
-// earlier is folded), so the lowest undelivered position can always go on.
+// Deadlock freedom: positions are claimed in order; a consumer frees its
+// slot before delivering, and waits only for the tile-fold slot it
+// delivers to (until the tile TS places earlier is folded, which needs only
+// lower positions), so the lowest undelivered position can always go on.
 // Every wait is bounded: a broken handshake ends the wave (wrong results),
 // it never hangs the GPU.
-constexpr int kPcProducers = 2, kPcConsumers = 8, kPcWaves = kPcProducers + kPcConsumers;
+constexpr int kPcProducers = 2;
+constexpr int pc_consumers(int ntok) { return ntok == 1 ? 12 : 8; }
+constexpr int pc_waves(int ntok) { return kPcProducers + pc_consumers(ntok); }
 constexpr int kPcSpin = 1 << 22;
 
 // s_waitcnt for vmcnt <= N (expcnt and lgkmcnt not waited for)
@@ -1210,26 +1288,32 @@ __device__ __forceinline__ void wait_vm() {
 // s_waitcnt lgkmcnt(0) (vmcnt and expcnt not waited for)
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
 
-typedef __attribute__((address_space(3))) volatile uint32_t* lsync_t;
-
-// Waits until *f == v, at most kPcSpin polls; false on time-out.
+// Waits until *f == v, at most kPcSpin polls; false on time-out.  The
+// polled word goes through readfirstlane so that the test is a scalar one:
+// every loop around a wait is then uniform to the compiler, which otherwise
+// may lower it as a divergent loop and run lanes in different iterations
+// (the claim in pc_consume relies on lane 0 being in every iteration).
 __device__ __forceinline__ bool spin_until(lsync_t f, uint32_t v) {
     for (int k = 0; k < kPcSpin; ++k) {
-        if (*f == v) return true;
+        if ((uint32_t)__builtin_amdgcn_readfirstlane(*f) == v) return true;
         __builtin_amdgcn_s_sleep(1);
     }
     return false;
 }
 
 // The LDS of one workgroup for tensor T.  Dynamic (offsets in bytes): R
-// weight slots of W bytes, RX x slots of X bytes, then the fold slots'
-// segment sums [TS][nseg][NTOK][32] floats.  Static (kq_pc_sync, words):
+// weight slots of W bytes; then x: RX slots of X bytes, or with resident x
+// (RX = 0) one X-byte slot per segment of a tile row (slot s holds blocks
+// 2s and 2s + 1); then the fold slots' segment sums [TS][nseg][NTOK][32]
+// floats.  Static (kq_pc_sync, words):
 // ready[R] (position + 1 once its weights and x are in), wdone[R] (position +
 // 1 once its weights are read into registers), xdone[RX] (once its x is no
-// longer read), owner[TS] and count[TS] of the fold slots.  The flags live
+// longer read), owner[TS] and count[TS] of the fold slots, the claim
+// counter, with resident x the consumers that have loaded their share of
+// it, and 64 sink words (lane0_word).  The flags live
 // in an array of their own, apart from the slots the direct loads write, so
 // polling them needs no wait for the loads in flight.
-constexpr int kPcMaxSlots = 16, kPcMaxFold = 8;
+constexpr int kPcMaxSlots = 24, kPcMaxFold = 16;
 struct PcLayout {
     int R, RX, TS, W, X, xs, sums;
     __device__ __forceinline__ PcLayout(const KqDesc& T, int w, int x) {
@@ -1239,10 +1323,11 @@ struct PcLayout {
         W = w;
         X = x;
         xs = R * W;
-        sums = xs + RX * X;
+        sums = xs + (RX ? RX : T.nseg) * X;
     }
     static constexpr int ready = 0, wdone = kPcMaxSlots, xdone = 2 * kPcMaxSlots, owner = 3 * kPcMaxSlots,
-                         count = 3 * kPcMaxSlots + kPcMaxFold, words = 3 * kPcMaxSlots + 2 * kPcMaxFold;
+                         count = 3 * kPcMaxSlots + kPcMaxFold, claim = 3 * kPcMaxSlots + 2 * kPcMaxFold,
+                         xready = claim + 1, sink = xready + 1, words = sink + 64;
 };
 
 // The steps of one producer: positions p, p + kPcProducers, ... of the run.
@@ -1250,43 +1335,47 @@ struct PcLayout {
 // weight slot and n - RX its x slot (R and RX are multiples of
 // kPcProducers of at least kPcProducers * D, so those positions are its own
 // and already published).
-template <class Col, int NTOK>
+template <class Col, int NTOK, bool XRES>
 __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, uint8_t* lds, lsync_t sync,
                                            const PcLayout& Y, int p) {
-    constexpr int D = 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4;     // steps in flight: D * LOADS <= 63
+    constexpr int LD = XRES ? Col::LOADS - 2 * NTOK : Col::LOADS;    // direct loads of one step
+    constexpr int D = 63 / LD < 4 ? 63 / LD : 4;                     // steps in flight: D * LD <= 63
     static_assert(D >= 2, "two steps in flight");
     typename Col::Offsets offs;
     offs.init(T);
     const int nseg = T.nseg;
     int issued = 0, published = 0;
     for (int n = p; n < nsteps; n += kPcProducers) {
-        const int ws = n % Y.R, xs = n % Y.RX;
+        const int ws = n % Y.R, xs = XRES ? 0 : n % Y.RX;
         if (n >= Y.R && !spin_until(sync + PcLayout::wdone + ws, (uint32_t)(n - Y.R + 1))) return;
-        if (n >= Y.RX && !spin_until(sync + PcLayout::xdone + xs, (uint32_t)(n - Y.RX + 1))) return;
+        if (!XRES && n >= Y.RX && !spin_until(sync + PcLayout::xdone + xs, (uint32_t)(n - Y.RX + 1))) return;
         const int j = j0 + n, tile = j / nseg, b = 2 * (j - tile * nseg);
         Col::dma_w(T, offs, tile, b, lds + ws * Y.W);
-        Col::dma_x(T, b, lds + Y.xs + xs * Y.X);
+        if (!XRES) Col::dma_x(T, b, lds + Y.xs + xs * Y.X);
         ++issued;
         if (issued - published == D) {
-            wait_vm<(D - 1) * Col::LOADS>();
+            wait_vm<(D - 1) * LD>();
             const int pos = p + kPcProducers * published;
-            if (kq_lane() == 0) sync[PcLayout::ready + pos % Y.R] = (uint32_t)(pos + 1);
+            lds_set(sync + PcLayout::ready + pos % Y.R, sync + PcLayout::sink, (uint32_t)(pos + 1));
             ++published;
         }
     }
     while (published < issued) {
         const int left = issued - published - 1;       // steps that may stay in flight
-        if (left >= 3) wait_vm<3 * Col::LOADS>();
-        else if (left == 2) wait_vm<2 * Col::LOADS>();
-        else if (left == 1) wait_vm<Col::LOADS>();
+        if (left >= 3) wait_vm<3 * LD>();
+        else if (left == 2) wait_vm<2 * LD>();
+        else if (left == 1) wait_vm<LD>();
         else wait_vm<0>();
         const int pos = p + kPcProducers * published;
-        if (kq_lane() == 0) sync[PcLayout::ready + pos % Y.R] = (uint32_t)(pos + 1);
+        lds_set(sync + PcLayout::ready + pos % Y.R, sync + PcLayout::sink, (uint32_t)(pos + 1));
         ++published;
     }
 }
 
-// The steps of one consumer: positions c, c + kPcConsumers, ... of the run.
+// One consumer (c = 0 .. pc_consumers(NTOK) - 1): with resident x, first
+// its share of x (pieces c, c + pc_consumers(NTOK), ... of 1 KB: one token plane of one
+// block of the segments the run reads, segment s in slot s % nseg), then
+// positions claimed in order until the run is done.
 template <class Col, int NTOK>
 __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint8_t* lds, lsync_t sync,
                                            const PcLayout& Y, int c) {
@@ -1294,21 +1383,38 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
     const int lane = kq_lane();
     const int nseg = T.nseg, nsteps = j1 - j0;
     const int first_owned = (j0 + nseg - 1) / nseg;     // first tile that lies wholly in the run
-    for (int n = c; n < nsteps; n += kPcConsumers) {
-        const int ws = n % Y.R, xs = n % Y.RX;
+    if (Y.RX == 0) {
+        const int need = min(nsteps, nseg), seg0 = j0 % nseg;
+        for (int q = c; q < need * 2 * NTOK; q += pc_consumers(NTOK)) {
+            const int k = q / (2 * NTOK), part = q - k * 2 * NTOK, kb = part / NTOK, t = part - kb * NTOK;
+            const int sg = seg0 + k < nseg ? seg0 + k : seg0 + k - nseg;
+            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (2 * sg + kb) + 4 * lane),
+                        lds + Y.xs + sg * Y.X + 1024 * part);
+        }
+        wait_vm<0>();
+        (void)lds_bump(sync + PcLayout::xready, sync + PcLayout::sink);
+        if (!spin_until(sync + PcLayout::xready, (uint32_t)pc_consumers(NTOK))) return;
+    }
+    for (;;) {
+        const int n = (int)lds_bump(sync + PcLayout::claim, sync + PcLayout::sink);
+        if (n >= nsteps) break;
+        const int ws = n % Y.R;
         if (!spin_until(sync + PcLayout::ready + ws, (uint32_t)(n + 1))) return;
         const int j = j0 + n, tile = j / nseg, seg = j - tile * nseg;
+        const int xs = Y.RX ? n % Y.RX : seg;
         typename Col::Regs regs;
         Col::load_regs(lds + ws * Y.W, regs);
         wait_lds();                                      // the block is in registers
-        if (lane == 0) sync[PcLayout::wdone + ws] = (uint32_t)(n + 1);
+        lds_set(sync + PcLayout::wdone + ws, sync + PcLayout::sink, (uint32_t)(n + 1));
         late_priority(t_start);
         float acc[NTOK];
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
         Col::compute_regs(regs, lds + Y.xs + xs * Y.X, acc);
-        wait_lds();                                      // every read of the x slot is done
-        if (lane == 0) sync[PcLayout::xdone + xs] = (uint32_t)(n + 1);
+        if (Y.RX) {
+            wait_lds();                                  // every read of the x slot is done
+            lds_set(sync + PcLayout::xdone + xs, sync + PcLayout::sink, (uint32_t)(n + 1));
+        }
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + dpp_xor1(acc[t]);     // the pair's two blocks
         if (tile * nseg >= j0 && (tile + 1) * nseg <= j1) {
@@ -1317,17 +1423,11 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
             const int ts = (tile - first_owned) % Y.TS;
             if (!spin_until(sync + PcLayout::owner + ts, (uint32_t)tile)) return;
             uint8_t* sums = lds + Y.sums + ((ts * nseg + seg) * NTOK) * 128;     // [TS][nseg][NTOK][32] floats
-            if ((lane & 1) == 0) {
+            // both lanes of a pair hold the pair sum: each stores it
 #pragma unroll
-                for (int t = 0; t < NTOK; ++t) reinterpret_cast<float*>(sums)[32 * t + (lane >> 1)] = acc[t];
-            }
+            for (int t = 0; t < NTOK; ++t) reinterpret_cast<float*>(sums)[32 * t + (lane >> 1)] = acc[t];
             wait_lds();
-            uint32_t old = 0;
-            if (lane == 0)
-                old = __hip_atomic_fetch_add((__attribute__((address_space(3))) uint32_t*)(sync + PcLayout::count + ts), 1u,
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-            old = __builtin_amdgcn_readfirstlane(old);
-            if (old == (uint32_t)(nseg - 1)) {
+            if (lds_bump(sync + PcLayout::count + ts, sync + PcLayout::sink) == (uint32_t)(nseg - 1)) {
                 float sum[NTOK];
 #pragma unroll
                 for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
@@ -1336,17 +1436,15 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
 #pragma unroll
                     for (int t = 0; t < NTOK; ++t) sum[t] = sum[t] + ss[32 * t + (lane >> 1)];
                 }
-                write_rows<NTOK, 32>(T, tile, sum);
+                write_rows_bf<NTOK>(T, tile, sum);
                 wait_lds();
-                if (lane == 0) {
-                    sync[PcLayout::count + ts] = 0u;
-                    sync[PcLayout::owner + ts] = (uint32_t)(tile + Y.TS);
-                }
+                lds_set(sync + PcLayout::count + ts, sync + PcLayout::sink, 0u);
+                lds_set(sync + PcLayout::owner + ts, sync + PcLayout::sink, (uint32_t)(tile + Y.TS));
             }
         } else {
             const int wslot = shared_slot(T, tile);
             store_partial<NTOK>(T, wslot, seg, acc);
-            arrive<NTOK, 32>(T, tile, wslot, 1);
+            arrive_bf<NTOK>(T, tile, wslot);
         }
     }
 }
@@ -1361,17 +1459,22 @@ __device__ __forceinline__ void pc_run(const KqDesc& T, int j0, int j1, uint8_t*
         sync[PcLayout::owner + k] = (uint32_t)(first_owned + k);
         sync[PcLayout::count + k] = 0u;
     }
+    if (threadIdx.x == 0) {
+        sync[PcLayout::claim] = 0u;
+        sync[PcLayout::xready] = 0u;
+    }
     __syncthreads();
     if (wave < kPcProducers) {
         __builtin_amdgcn_s_setprio(3);
-        pc_produce<Col, NTOK>(T, j0, j1 - j0, lds, sync, Y, wave);
+        if (Y.RX == 0) pc_produce<Col, NTOK, true>(T, j0, j1 - j0, lds, sync, Y, wave);
+        else pc_produce<Col, NTOK, false>(T, j0, j1 - j0, lds, sync, Y, wave);
     } else {
         pc_consume<Col, NTOK>(T, j0, j1, lds, sync, Y, wave - kPcProducers);
     }
 }
 
 template <int NTOK>
-__global__ __launch_bounds__(64 * kPcWaves, 1) void kq_pc_kernel(const KqLaunch L) {
+__global__ __launch_bounds__(64 * pc_waves(NTOK), 1) void kq_pc_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_pc_lds[];
     __shared__ uint32_t kq_pc_sync[PcLayout::words];
     uint8_t* lds = reinterpret_cast<uint8_t*>(kq_pc_lds);
@@ -1398,13 +1501,13 @@ __global__ __launch_bounds__(64 * kPcWaves, 1) void kq_pc_kernel(const KqLaunch 
 }
 
 // The pipelined kernel's sizes for a tensor of this format at ntok (1 or
-// 2): LDS bytes of a step's weights (*w) and x (*x), and D, the steps a
-// producer keeps in flight.
+// 2): LDS bytes of a step's weights (*w) and x (*x), and the direct loads
+// of a step with x streamed (*loads; 2 * ntok fewer with x resident).
 template <class Col>
 static void pc_sizes_t(int* w, int* x, int* d) {
     *w = Col::PC_W;
     *x = Col::PC_X;
-    *d = 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4;
+    *d = Col::LOADS;
 }
 void pc_sizes(int32_t fmt, int32_t ntok, int* w, int* x, int* d) {
     if (ntok == 1) {
@@ -2100,25 +2203,39 @@ int plan_pipelined(KqLaunch* L) {
         lm = -1;
     if (lm < 0) return 0;
     const int budget = lm - (int)sizeof(uint32_t) * PcLayout::words - 64;
-    constexpr int TS = 3;
     int lds = 0;
     for (int i = 0; i < L->h.n; ++i) {
         if (L->t[i].tile_rows != 32) return 0;
     }
     for (int i = 0; i < L->h.n; ++i) {
         KqDesc& D = L->t[i];
-        int wb = 0, xb = 0, d = 0;
-        pc_sizes(D.fmt, L->ntok, &wb, &xb, &d);
-        // x slots: twice the steps both producers keep in flight (held while
-        // a step computes); weight slots: as many as the rest of the LDS
-        // holds (freed as soon as a consumer has its block in registers)
-        const int RX = 4 * d;
+        int wb = 0, xb = 0, loads = 0;
+        pc_sizes(D.fmt, L->ntok, &wb, &xb, &loads);
+        // fold slots: enough tiles for the positions the consumers hold at
+        // once, plus two
+        const int nc = pc_consumers(L->ntok);
+        const int TS = min(kPcMaxFold, 2 + (nc + D.nseg - 1) / D.nseg);
+        const auto depth = [](int ld) { return 63 / ld < 4 ? 63 / ld : 4; };     // as pc_produce's D
         const int sums = TS * D.nseg * L->ntok * 128;
-        int R = (budget - sums - RX * xb) / wb;
-        R = (R > kPcMaxSlots ? kPcMaxSlots : R) & ~1;
-        if (R < 2 * d || RX > kPcMaxSlots) return 0;
-        D.reserved0 = R | (TS << 8) | (RX << 16);
-        const int need = R * wb + RX * xb + sums;
+        const auto wslots = [&](int x_bytes) {    // weight slots: what the rest of the LDS holds, even
+            const int r = (budget - sums - x_bytes) / wb;
+            return (r > kPcMaxSlots ? kPcMaxSlots : r) & ~1;
+        };
+        // resident x if it leaves room for both producers' steps in flight
+        // twice over; else an x ring of the steps in flight plus one a
+        // consumer (x is held while a step computes)
+        const int d_res = depth(loads - 2 * L->ntok), x_res = D.nseg * xb, R_res = wslots(x_res);
+        const int d = depth(loads), RX = (2 * d + nc + 1) & ~1, R = wslots(RX * xb);
+        int need = 0;
+        if (R_res >= 2 * d_res) {
+            D.reserved0 = R_res | (TS << 8);
+            need = R_res * wb + x_res + sums;
+        } else if (R >= 2 * d && RX <= kPcMaxSlots) {
+            D.reserved0 = R | (TS << 8) | (RX << 16);
+            need = R * wb + RX * xb + sums;
+        } else {
+            return 0;
+        }
         if (need > lds) lds = need;
     }
     L->lds_bytes = lds;
@@ -2150,9 +2267,8 @@ int launch_matvec(const KqLaunch& L, hipStream_t stream) {
     const dim3 grid((unsigned)L.grid), block(64);
     const size_t lds = (size_t)L.lds_bytes;
     if (L.pipelined) {
-        const dim3 pblock(64 * kPcWaves);
-        if (L.ntok == 1) hipLaunchKernelGGL(kq_pc_kernel<1>, grid, pblock, lds, stream, L);
-        else hipLaunchKernelGGL(kq_pc_kernel<2>, grid, pblock, lds, stream, L);
+        if (L.ntok == 1) hipLaunchKernelGGL(kq_pc_kernel<1>, grid, dim3(64 * pc_waves(1)), lds, stream, L);
+        else hipLaunchKernelGGL(kq_pc_kernel<2>, grid, dim3(64 * pc_waves(2)), lds, stream, L);
         return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
     }
     switch (L.ntok) {
