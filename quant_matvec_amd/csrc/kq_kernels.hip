@@ -437,11 +437,12 @@ struct K45Pair {
     };
     uint4 stg[N];
     XStage<NTOK> xs0, xs1;
-    // ---- the pipelined kernel's pieces: the step's weights (in commit()'s
-    // layout, chunk q at byte 16q) and its x (block b, then b+1) go to
-    // separate LDS slots by direct loads; a consumer reads its lane's block
-    // into registers, frees the weight slot, and computes from registers
-    static constexpr int LOADS = N + 2 * NTOK;                 // direct loads of one step
+    // ---- the pipelined kernel's pieces: the step's weights go to an LDS
+    // slot by direct loads, in commit()'s layout (chunk q at byte 16q); x
+    // (block b, then b+1, one plane per token) sits in a slot of its own; a
+    // consumer reads its lane's block into registers, frees the weight
+    // slot, and computes from registers
+    static constexpr int LOADS = N;                            // direct loads of one step
     static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
@@ -449,14 +450,6 @@ struct K45Pair {
         gbytes_t col = gbytes(T.w) + (size_t)tile * TR * T.row_bytes + (size_t)b * BB;
 #pragma unroll
         for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
-    }
-    static __device__ __forceinline__ void dma_x(const KqDesc& T, int b, uint8_t* xslot) {
-        const int lane = kq_lane();
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) {
-            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane), xslot + 1024 * t);
-            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (b + 1) + 4 * lane), xslot + 1024 * (NTOK + t));
-        }
     }
     struct Regs {
         uint4 v[C];
@@ -824,7 +817,7 @@ struct Q6Pair {
     // (lane & 31) lands at word `lane` of its array (lanes 32..63 repeat
     // rows 0..31); a lane's block is 53 aligned words, shifted 16 bits for
     // the pair's second block
-    static constexpr int LOADS = N + 1 + 2 * NTOK;             // direct loads of one step
+    static constexpr int LOADS = N + 1;                        // direct loads of one step
     static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
@@ -835,14 +828,6 @@ struct Q6Pair {
 #pragma unroll
         for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
         kq::dma<4>(col + min(o.off104, max104), wslot + TR * ROWB);
-    }
-    static __device__ __forceinline__ void dma_x(const KqDesc& T, int b, uint8_t* xslot) {
-        const int lane = kq_lane();
-#pragma unroll
-        for (int t = 0; t < NTOK; ++t) {
-            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * b + 4 * lane), xslot + 1024 * t);
-            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (b + 1) + 4 * lane), xslot + 1024 * (NTOK + t));
-        }
     }
     struct Regs {
         uint32_t wd[53];
@@ -1245,21 +1230,20 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // ------------------------------------------------------------ the pipelined kernel
 // Launches whose tensors all run in 32-row tiles with two-block segments
 // (every decode set and every large matrix at one token plane, at two up to
-// 16384 rows) take this kernel: one workgroup a compute unit, holding two
-// kinds of waves.
+// 16384 rows) and whose x fits in LDS beside a full ring take this kernel:
+// one workgroup a compute unit, holding two kinds of waves.
 //   * Producers (kPcProducers) only move bytes.  A producer issues the direct
 //     global -> LDS loads of its steps into a ring of LDS slots, keeps several
 //     steps in flight, waits for the oldest with vmcnt and publishes its slot.
-//   * Consumers (pc_consumers(NTOK): 12 at one token plane, whose registers
-//     allow four waves a SIMD, else 8) only compute.  A free consumer claims the
+//   * Consumers (kPcConsumers: 12, four waves a SIMD with the producers
+//     within the kernel's 128 registers) only compute.  A free consumer claims the
 //     next position of the workgroup's run (an LDS counter), waits for its
 //     slot, copies its lane's block into registers, frees the slot and
 //     computes the step exactly as kq_matvec_kernel does.  Claiming in
 //     order, rather than a fixed share per consumer, frees each slot as soon
 //     as any consumer is idle.
-// x is either resident (every x block the run reads, loaded once at the
-// start, when it fits beside the weight ring) or streamed with each step
-// into a ring of its own, held until the step's products are done.
+// x is resident: every x block the run reads, loaded once at the start by
+// the consumers.
 // So no wave waits to issue a load while it holds data to compute, and the
 // run's bytes are requested as fast as the ring frees.  Position n of the
 // run is segment j0 + n (one step: 32 rows x 2 blocks) in slot n % R.  The
@@ -1274,9 +1258,7 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // lower positions), so the lowest undelivered position can always go on.
 // Every wait is bounded: a broken handshake ends the wave (wrong results),
 // it never hangs the GPU.
-constexpr int kPcProducers = 2;
-constexpr int pc_consumers(int ntok) { return ntok == 1 ? 12 : 8; }
-constexpr int pc_waves(int ntok) { return kPcProducers + pc_consumers(ntok); }
+constexpr int kPcProducers = 2, kPcConsumers = 12, kPcWaves = kPcProducers + kPcConsumers;
 constexpr int kPcSpin = 1 << 22;
 
 // s_waitcnt for vmcnt <= N (expcnt and lgkmcnt not waited for)
@@ -1302,56 +1284,52 @@ __device__ __forceinline__ bool spin_until(lsync_t f, uint32_t v) {
 }
 
 // The LDS of one workgroup for tensor T.  Dynamic (offsets in bytes): R
-// weight slots of W bytes; then x: RX slots of X bytes, or with resident x
-// (RX = 0) one X-byte slot per segment of a tile row (slot s holds blocks
-// 2s and 2s + 1); then the fold slots' segment sums [TS][nseg][NTOK][32]
-// floats.  Static (kq_pc_sync, words):
-// ready[R] (position + 1 once its weights and x are in), wdone[R] (position +
-// 1 once its weights are read into registers), xdone[RX] (once its x is no
-// longer read), owner[TS] and count[TS] of the fold slots, the claim
-// counter, with resident x the consumers that have loaded their share of
-// it, and 64 sink words (lane0_word).  The flags live
-// in an array of their own, apart from the slots the direct loads write, so
-// polling them needs no wait for the loads in flight.
-constexpr int kPcMaxSlots = 24, kPcMaxFold = 16;
+// weight slots of W bytes; x, one X-byte slot per segment of a tile row
+// (slot s holds blocks 2s and 2s + 1); then the fold slots' segment sums
+// [TS][nseg][NTOK][32] floats.  Static (kq_pc_sync, words): ready[R]
+// (position + 1 once its weights are in), wdone[R] (position + 1 once its
+// weights are read into registers), owner[TS] and count[TS] of the fold
+// slots, the claim counter, the consumers that have loaded their share of x,
+// and 64 sink words (lane0_word).  The flags live in an array of their own,
+// apart from the slots the direct loads write, so polling them needs no
+// wait for the loads in flight.
+constexpr int kPcMaxSlots = 16, kPcMaxFold = 16;
 struct PcLayout {
-    int R, RX, TS, W, X, xs, sums;
+    int R, TS, W, X, xs, sums;
     __device__ __forceinline__ PcLayout(const KqDesc& T, int w, int x) {
         R = T.reserved0 & 255;
         TS = (T.reserved0 >> 8) & 255;
-        RX = (T.reserved0 >> 16) & 255;
         W = w;
         X = x;
         xs = R * W;
-        sums = xs + (RX ? RX : T.nseg) * X;
+        sums = xs + T.nseg * X;
     }
-    static constexpr int ready = 0, wdone = kPcMaxSlots, xdone = 2 * kPcMaxSlots, owner = 3 * kPcMaxSlots,
-                         count = 3 * kPcMaxSlots + kPcMaxFold, claim = 3 * kPcMaxSlots + 2 * kPcMaxFold,
-                         xready = claim + 1, sink = xready + 1, words = sink + 64;
+    static constexpr int ready = 0, wdone = kPcMaxSlots, owner = 2 * kPcMaxSlots, count = owner + kPcMaxFold,
+                         claim = count + kPcMaxFold, xready = claim + 1, sink = xready + 1, words = sink + 64;
 };
+
+// Steps a producer keeps in flight: D * LOADS <= 63 (vmcnt), at most 4.
+template <class Col>
+constexpr int pc_depth() { return 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4; }
 
 // The steps of one producer: positions p, p + kPcProducers, ... of the run.
 // Before issuing position n it waits until position n - R has left its
-// weight slot and n - RX its x slot (R and RX are multiples of
-// kPcProducers of at least kPcProducers * D, so those positions are its own
-// and already published).
-template <class Col, int NTOK, bool XRES>
+// slot (R is a multiple of kPcProducers of at least kPcProducers * D, so
+// that position is its own and already published).
+template <class Col, int NTOK>
 __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, uint8_t* lds, lsync_t sync,
                                            const PcLayout& Y, int p) {
-    constexpr int LD = XRES ? Col::LOADS - 2 * NTOK : Col::LOADS;    // direct loads of one step
-    constexpr int D = 63 / LD < 4 ? 63 / LD : 4;                     // steps in flight: D * LD <= 63
+    constexpr int LD = Col::LOADS, D = pc_depth<Col>();
     static_assert(D >= 2, "two steps in flight");
     typename Col::Offsets offs;
     offs.init(T);
     const int nseg = T.nseg;
     int issued = 0, published = 0;
     for (int n = p; n < nsteps; n += kPcProducers) {
-        const int ws = n % Y.R, xs = XRES ? 0 : n % Y.RX;
+        const int ws = n % Y.R;
         if (n >= Y.R && !spin_until(sync + PcLayout::wdone + ws, (uint32_t)(n - Y.R + 1))) return;
-        if (!XRES && n >= Y.RX && !spin_until(sync + PcLayout::xdone + xs, (uint32_t)(n - Y.RX + 1))) return;
         const int j = j0 + n, tile = j / nseg, b = 2 * (j - tile * nseg);
         Col::dma_w(T, offs, tile, b, lds + ws * Y.W);
-        if (!XRES) Col::dma_x(T, b, lds + Y.xs + xs * Y.X);
         ++issued;
         if (issued - published == D) {
             wait_vm<(D - 1) * LD>();
@@ -1372,10 +1350,10 @@ __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, 
     }
 }
 
-// One consumer (c = 0 .. pc_consumers(NTOK) - 1): with resident x, first
-// its share of x (pieces c, c + pc_consumers(NTOK), ... of 1 KB: one token plane of one
-// block of the segments the run reads, segment s in slot s % nseg), then
-// positions claimed in order until the run is done.
+// One consumer (c = 0 .. kPcConsumers - 1): first its share of x (pieces
+// c, c + kPcConsumers, ... of 1 KB: one token plane of one block of the
+// segments the run reads, segment s in slot s % nseg), then positions
+// claimed in order until the run is done.
 template <class Col, int NTOK>
 __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint8_t* lds, lsync_t sync,
                                            const PcLayout& Y, int c) {
@@ -1383,9 +1361,9 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
     const int lane = kq_lane();
     const int nseg = T.nseg, nsteps = j1 - j0;
     const int first_owned = (j0 + nseg - 1) / nseg;     // first tile that lies wholly in the run
-    if (Y.RX == 0) {
+    {
         const int need = min(nsteps, nseg), seg0 = j0 % nseg;
-        for (int q = c; q < need * 2 * NTOK; q += pc_consumers(NTOK)) {
+        for (int q = c; q < need * 2 * NTOK; q += kPcConsumers) {
             const int k = q / (2 * NTOK), part = q - k * 2 * NTOK, kb = part / NTOK, t = part - kb * NTOK;
             const int sg = seg0 + k < nseg ? seg0 + k : seg0 + k - nseg;
             kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (2 * sg + kb) + 4 * lane),
@@ -1393,7 +1371,7 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
         }
         wait_vm<0>();
         (void)lds_bump(sync + PcLayout::xready, sync + PcLayout::sink);
-        if (!spin_until(sync + PcLayout::xready, (uint32_t)pc_consumers(NTOK))) return;
+        if (!spin_until(sync + PcLayout::xready, (uint32_t)kPcConsumers)) return;
     }
     for (;;) {
         const int n = (int)lds_bump(sync + PcLayout::claim, sync + PcLayout::sink);
@@ -1401,7 +1379,6 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
         const int ws = n % Y.R;
         if (!spin_until(sync + PcLayout::ready + ws, (uint32_t)(n + 1))) return;
         const int j = j0 + n, tile = j / nseg, seg = j - tile * nseg;
-        const int xs = Y.RX ? n % Y.RX : seg;
         typename Col::Regs regs;
         Col::load_regs(lds + ws * Y.W, regs);
         wait_lds();                                      // the block is in registers
@@ -1410,11 +1387,7 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
         float acc[NTOK];
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) acc[t] = 0.0f;
-        Col::compute_regs(regs, lds + Y.xs + xs * Y.X, acc);
-        if (Y.RX) {
-            wait_lds();                                  // every read of the x slot is done
-            lds_set(sync + PcLayout::xdone + xs, sync + PcLayout::sink, (uint32_t)(n + 1));
-        }
+        Col::compute_regs(regs, lds + Y.xs + seg * Y.X, acc);
 #pragma unroll
         for (int t = 0; t < NTOK; ++t) acc[t] = acc[t] + dpp_xor1(acc[t]);     // the pair's two blocks
         if (tile * nseg >= j0 && (tile + 1) * nseg <= j1) {
@@ -1454,7 +1427,7 @@ __device__ __forceinline__ void pc_run(const KqDesc& T, int j0, int j1, uint8_t*
     const PcLayout Y(T, Col::PC_W, Col::PC_X);
     // flags zero, fold slots owned by the run's first TS whole tiles
     const int first_owned = (j0 + T.nseg - 1) / T.nseg;
-    for (int k = threadIdx.x; k < 3 * kPcMaxSlots; k += blockDim.x) sync[k] = 0u;
+    for (int k = threadIdx.x; k < 2 * kPcMaxSlots; k += blockDim.x) sync[k] = 0u;
     for (int k = threadIdx.x; k < kPcMaxFold; k += blockDim.x) {
         sync[PcLayout::owner + k] = (uint32_t)(first_owned + k);
         sync[PcLayout::count + k] = 0u;
@@ -1466,15 +1439,14 @@ __device__ __forceinline__ void pc_run(const KqDesc& T, int j0, int j1, uint8_t*
     __syncthreads();
     if (wave < kPcProducers) {
         __builtin_amdgcn_s_setprio(3);
-        if (Y.RX == 0) pc_produce<Col, NTOK, true>(T, j0, j1 - j0, lds, sync, Y, wave);
-        else pc_produce<Col, NTOK, false>(T, j0, j1 - j0, lds, sync, Y, wave);
+        pc_produce<Col, NTOK>(T, j0, j1 - j0, lds, sync, Y, wave);
     } else {
         pc_consume<Col, NTOK>(T, j0, j1, lds, sync, Y, wave - kPcProducers);
     }
 }
 
 template <int NTOK>
-__global__ __launch_bounds__(64 * pc_waves(NTOK), 1) void kq_pc_kernel(const KqLaunch L) {
+__global__ __launch_bounds__(64 * kPcWaves, 1) void kq_pc_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_pc_lds[];
     __shared__ uint32_t kq_pc_sync[PcLayout::words];
     uint8_t* lds = reinterpret_cast<uint8_t*>(kq_pc_lds);
@@ -1501,13 +1473,13 @@ __global__ __launch_bounds__(64 * pc_waves(NTOK), 1) void kq_pc_kernel(const KqL
 }
 
 // The pipelined kernel's sizes for a tensor of this format at ntok (1 or
-// 2): LDS bytes of a step's weights (*w) and x (*x), and the direct loads
-// of a step with x streamed (*loads; 2 * ntok fewer with x resident).
+// 2): LDS bytes of a step's weights (*w) and of a segment's x (*x), and the
+// steps a producer keeps in flight (*d).
 template <class Col>
 static void pc_sizes_t(int* w, int* x, int* d) {
     *w = Col::PC_W;
     *x = Col::PC_X;
-    *d = Col::LOADS;
+    *d = pc_depth<Col>();
 }
 void pc_sizes(int32_t fmt, int32_t ntok, int* w, int* x, int* d) {
     if (ntok == 1) {
@@ -2209,33 +2181,19 @@ int plan_pipelined(KqLaunch* L) {
     }
     for (int i = 0; i < L->h.n; ++i) {
         KqDesc& D = L->t[i];
-        int wb = 0, xb = 0, loads = 0;
-        pc_sizes(D.fmt, L->ntok, &wb, &xb, &loads);
-        // fold slots: enough tiles for the positions the consumers hold at
-        // once, plus two
-        const int nc = pc_consumers(L->ntok);
-        const int TS = min(kPcMaxFold, 2 + (nc + D.nseg - 1) / D.nseg);
-        const auto depth = [](int ld) { return 63 / ld < 4 ? 63 / ld : 4; };     // as pc_produce's D
-        const int sums = TS * D.nseg * L->ntok * 128;
-        const auto wslots = [&](int x_bytes) {    // weight slots: what the rest of the LDS holds, even
-            const int r = (budget - sums - x_bytes) / wb;
-            return (r > kPcMaxSlots ? kPcMaxSlots : r) & ~1;
-        };
-        // resident x if it leaves room for both producers' steps in flight
-        // twice over; else an x ring of the steps in flight plus one a
-        // consumer (x is held while a step computes)
-        const int d_res = depth(loads - 2 * L->ntok), x_res = D.nseg * xb, R_res = wslots(x_res);
-        const int d = depth(loads), RX = (2 * d + nc + 1) & ~1, R = wslots(RX * xb);
-        int need = 0;
-        if (R_res >= 2 * d_res) {
-            D.reserved0 = R_res | (TS << 8);
-            need = R_res * wb + x_res + sums;
-        } else if (R >= 2 * d && RX <= kPcMaxSlots) {
-            D.reserved0 = R | (TS << 8) | (RX << 16);
-            need = R * wb + RX * xb + sums;
-        } else {
-            return 0;
-        }
+        int wb = 0, xb = 0, d = 0;
+        pc_sizes(D.fmt, L->ntok, &wb, &xb, &d);
+        // fold slots: the tiles the consumers' positions can span, plus two
+        const int TS = min(kPcMaxFold, 2 + (kPcConsumers + D.nseg - 1) / D.nseg);
+        const int sums = TS * D.nseg * L->ntok * 128, x_bytes = D.nseg * xb;
+        // weight slots: what the rest of the LDS holds (even, at most
+        // kPcMaxSlots), at least every producer's steps in flight, or the
+        // launch takes kq_matvec_kernel
+        int R = (budget - sums - x_bytes) / wb;
+        R = (R > kPcMaxSlots ? kPcMaxSlots : R) & ~1;
+        if (R < kPcProducers * d) return 0;
+        D.reserved0 = R | (TS << 8);
+        const int need = R * wb + x_bytes + sums;
         if (need > lds) lds = need;
     }
     L->lds_bytes = lds;
@@ -2267,8 +2225,8 @@ int launch_matvec(const KqLaunch& L, hipStream_t stream) {
     const dim3 grid((unsigned)L.grid), block(64);
     const size_t lds = (size_t)L.lds_bytes;
     if (L.pipelined) {
-        if (L.ntok == 1) hipLaunchKernelGGL(kq_pc_kernel<1>, grid, dim3(64 * pc_waves(1)), lds, stream, L);
-        else hipLaunchKernelGGL(kq_pc_kernel<2>, grid, dim3(64 * pc_waves(2)), lds, stream, L);
+        if (L.ntok == 1) hipLaunchKernelGGL(kq_pc_kernel<1>, grid, dim3(64 * kPcWaves), lds, stream, L);
+        else hipLaunchKernelGGL(kq_pc_kernel<2>, grid, dim3(64 * kPcWaves), lds, stream, L);
         return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
     }
     switch (L.ntok) {

@@ -277,13 +277,19 @@ def test_stream52_all_layers_all_rows():
 
 PIPE_CASES = [
     ("qkvg set", [(Q4_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0), (Q6_K, 256, 6656, 0), (Q4_K, 4096, 6656, 0)], 1),
-    ("q5 set ntok2", [(Q5_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0)], 2),
+    ("q5 set ntok2", [(Q5_K, 4096, 6656, 0), (Q4_K, 256, 6656, 0)], 2),
     ("kv pair small", [(Q6_K, 256, 6656, 0), (Q5_K, 256, 6656, 1)], 1),
     ("ragged large", [(Q6_K, 20037, 6656, 0)], 1),
     ("short rows", [(Q4_K, 3000, 512, 0), (Q5_K, 77, 1024, 1), (Q6_K, 1, 256, 2)], 2),
+    ("one-block segments", [(Q6_K, 16448, 512, 0), (Q4_K, 37, 512, 1)], 1),
+    # one-wave kernel: odd blocks; x beside a ring does not fit (long rows,
+    # Q6_K at two token planes)
+    ("mixed plans", [(Q4_K, 4096, 6656, 0), (Q6_K, 300, 2304, 1)], 1),
     ("long rows", [(Q4_K, 2050, 19968, 0)], 1),
-    ("mixed plans", [(Q4_K, 4096, 6656, 0), (Q6_K, 300, 2304, 1)], 1),     # odd blocks: one-wave kernel
+    ("q6 ntok2", [(Q6_K, 4096, 6656, 0)], 2),
 ]
+ONE_WAVE_CASES = ("mixed plans", "long rows", "q6 ntok2")
+PC_CASES = ("qkvg set", "q5 set ntok2", "kv pair small", "ragged large", "one-block segments")
 
 
 @pytest.mark.parametrize("name,specs,ntok", PIPE_CASES, ids=[c[0] for c in PIPE_CASES])
@@ -305,9 +311,9 @@ def test_pipelined_kernel_bitwise_equals_one_wave_kernel(name, specs, ntok):
             members = kq.make_set([dict(fmt=f, w=dw, x=dxs[xi], y=y, rows=r, cols=c, ldx=xcols[xi])
                                    for (f, r, c, xi), dw, y in zip(specs, dws, ys)])
             kernel = kq.kq_debug_plan_kernel(members, ntok=ntok)
-            if not pipe or name == "mixed plans":
+            if not pipe or name in ONE_WAVE_CASES:
                 assert kernel == "kq_matvec_kernel<%d>" % ntok, kernel
-            elif name in ("qkvg set", "q5 set ntok2", "ragged large", "long rows"):
+            elif name in PC_CASES:
                 assert kernel == "kq_pc_kernel<%d>" % ntok, kernel
             kq.kq_matvec_set(members, ntok=ntok)
             outs[pipe] = [host(y) for y in ys]
