@@ -1018,18 +1018,18 @@ __device__ __forceinline__ void write_rows_bf(const KqDesc& T, int tile, const f
     }
 }
 
-// arrive(T, tile, slot, 1) for a 32-row tile, branch-free.
+// arrive(T, tile, slot, count) for a 32-row tile, branch-free.
 template <int NTOK>
-__device__ __forceinline__ void arrive_bf(const KqDesc& T, int tile, int slot) {
+__device__ __forceinline__ void arrive_bf(const KqDesc& T, int tile, int slot, int count) {
     __attribute__((address_space(1))) uint32_t* ctr = (__attribute__((address_space(1))) uint32_t*)(T.counters + slot);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     __builtin_amdgcn_s_waitcnt(0);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
     const __amdgpu_buffer_rsrc_t c = __builtin_amdgcn_make_buffer_rsrc(T.counters + slot, (short)0, 4, kBufFlags);
-    uint32_t old = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(1, c, kq_lane() == 0 ? 0u : kBufDrop, 0, 0);
+    uint32_t old = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(count, c, kq_lane() == 0 ? 0u : kBufDrop, 0, 0);
     old = __builtin_amdgcn_readfirstlane(old);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    if (old + 1u != (uint32_t)T.nseg) return;
+    if (old + (uint32_t)count != (uint32_t)T.nseg) return;
     float sum[NTOK];
     sum_partials<NTOK>(T, slot, sum);
     write_rows_bf<NTOK>(T, tile, sum);
@@ -1331,7 +1331,13 @@ __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, 
         const int j = j0 + n, tile = j / nseg, b = 2 * (j - tile * nseg);
         Col::dma_w(T, offs, tile, b, lds + ws * Y.W);
         ++issued;
-        if (issued - published == D) {
+        // the first step is published once the second is issued (the
+        // consumers start sooner), the others with D steps in flight
+        if (published == 0 && issued == 2) {
+            wait_vm<LD>();
+            lds_set(sync + PcLayout::ready + p % Y.R, sync + PcLayout::sink, (uint32_t)(p + 1));
+            ++published;
+        } else if (issued - published == D) {
             wait_vm<(D - 1) * LD>();
             const int pos = p + kPcProducers * published;
             lds_set(sync + PcLayout::ready + pos % Y.R, sync + PcLayout::sink, (uint32_t)(pos + 1));
@@ -1395,19 +1401,18 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
             // the tile TS places earlier has been folded
             const int ts = (tile - first_owned) % Y.TS;
             if (!spin_until(sync + PcLayout::owner + ts, (uint32_t)tile)) return;
-            uint8_t* sums = lds + Y.sums + ((ts * nseg + seg) * NTOK) * 128;     // [TS][nseg][NTOK][32] floats
+            float* sums = reinterpret_cast<float*>(lds + Y.sums) + ts * nseg * NTOK * 32;    // [TS][nseg][NTOK][32]
             // both lanes of a pair hold the pair sum: each stores it
 #pragma unroll
-            for (int t = 0; t < NTOK; ++t) reinterpret_cast<float*>(sums)[32 * t + (lane >> 1)] = acc[t];
+            for (int t = 0; t < NTOK; ++t) sums[(seg * NTOK + t) * 32 + (lane >> 1)] = acc[t];
             wait_lds();
             if (lds_bump(sync + PcLayout::count + ts, sync + PcLayout::sink) == (uint32_t)(nseg - 1)) {
                 float sum[NTOK];
 #pragma unroll
                 for (int t = 0; t < NTOK; ++t) sum[t] = 0.0f;
                 for (int s2 = 0; s2 < nseg; ++s2) {
-                    const float* ss = reinterpret_cast<const float*>(lds + Y.sums + ((ts * nseg + s2) * NTOK) * 128);
 #pragma unroll
-                    for (int t = 0; t < NTOK; ++t) sum[t] = sum[t] + ss[32 * t + (lane >> 1)];
+                    for (int t = 0; t < NTOK; ++t) sum[t] = sum[t] + sums[(s2 * NTOK + t) * 32 + (lane >> 1)];
                 }
                 write_rows_bf<NTOK>(T, tile, sum);
                 wait_lds();
@@ -1415,9 +1420,11 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
                 lds_set(sync + PcLayout::owner + ts, sync + PcLayout::sink, (uint32_t)(tile + Y.TS));
             }
         } else {
+            // a tile shared with other workgroups: straight to the workspace
+            // (the round trips of different segments overlap)
             const int wslot = shared_slot(T, tile);
             store_partial<NTOK>(T, wslot, seg, acc);
-            arrive_bf<NTOK>(T, tile, wslot);
+            arrive_bf<NTOK>(T, tile, wslot, 1);
         }
     }
 }
