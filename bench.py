@@ -34,17 +34,49 @@ KERNEL_SOURCES = ["quant_matvec_amd/csrc/kq_kernels.hip", "quant_matvec_amd/csrc
                   "quant_matvec_amd/csrc/kq_plan.h", "quant_matvec_amd/csrc/kq_decode.h", "include/kqmv.h"]
 
 
-def measured_traffic(wname):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary of this workload, or None when there is none or the kernel
-    sources have changed since it was taken."""
-    import glob
+def code_only(text):
+    """C/C++ source with its comments removed and its whitespace runs
+    collapsed: what the compiler sees, so that a comment edit does not
+    unlink a counter measurement from the kernel it measured."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                 # string or char literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
+def kernel_sources_digest():
+    """16 hex digits of sha256 over the kernel sources' code (comments and
+    whitespace runs excluded), in KERNEL_SOURCES order."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
-    digest = h.hexdigest()[:16]
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(wname):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary of this workload, or None when there is none or the kernel
+    sources' code has changed since it was taken."""
+    import glob
+    digest = kernel_sources_digest()
     for path in glob.glob(os.path.join(ROOT, "profiles", "*_hbm_traffic.md")):
         with open(path) as fh:
             for line in fh:
@@ -91,7 +123,7 @@ def build_workload(name, ntok):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
     import torch

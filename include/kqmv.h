@@ -255,14 +255,17 @@ int kq_dequant(int32_t fmt, const void* w, int64_t rows, int64_t cols,
 int kq_debug_read_probe(const void* buf, int64_t bytes, void* sink, void* stream);
 
 /*
- * Debug/test export: on = 0 makes kq_matvec, kq_matvec_set and
- * kq_matvec_set_noalloc use only the one-wave-workgroup kernel; on = 1
- * (the default, unless the environment sets KQMV_PIPELINE=0) lets launches
- * whose tensors all run in 32-row tiles at ntok <= 2 take the pipelined
- * producer/consumer kernel.  Both give the same bits.  Process-wide; not
- * for use while other threads launch.  Returns KQ_OK.
+ * Debug/test export: which launches of kq_matvec, kq_matvec_set and
+ * kq_matvec_set_noalloc may take the pipelined producer/consumer kernel
+ * instead of the one-wave-workgroup kernel.  mode = 0: none; mode = 1 (the
+ * default, unless the environment sets KQMV_PIPELINE=0): launches whose
+ * tensors all run in 32-row tiles at ntok <= 2 and that have at least four
+ * segment steps a compute unit; mode = 2: such launches of any size (for
+ * tests of small shapes).  Values below 0 act as 0, above 2 as 2.  Both
+ * kernels give the same bits.  Process-wide; not for use while other
+ * threads launch.  Returns KQ_OK.
  */
-int kq_debug_set_pipeline(int32_t on);
+int kq_debug_set_pipeline(int32_t mode);
 
 /*
  * Debug/test export: which kernel kq_matvec_set would launch for this set
@@ -272,6 +275,28 @@ int kq_debug_set_pipeline(int32_t on);
  * descriptors (not the buffers they point to).
  */
 int kq_debug_plan_kernel(const kq_tensor* tensors, int32_t n, int32_t ntok);
+
+/*
+ * Debug/test export: token-plane groups of kq_matvec, kq_matvec_set and
+ * kq_matvec_set_noalloc.  A launch at ntok >= 3 with few segments splits
+ * each tensor's ntok planes into G groups of ntok / G planes, run as
+ * separate members of the one launch with the plan of the full ntok (more
+ * workgroups share the compute; each group reads the weights again).
+ * groups = 0 (the default): G chosen per launch from the segment count,
+ * the resident workgroups of the device and ntok (G = 1 at ntok <= 2).
+ * groups >= 1: G = groups wherever it divides ntok and
+ * n * groups <= 16, else 1 (for tests).  Negative values act as 0.  Every
+ * G gives the same bits.  Process-wide; not for use while other threads
+ * launch.  Returns KQ_OK.
+ */
+int kq_debug_set_plane_groups(int32_t groups);
+
+/*
+ * Debug/test export: the token-plane groups G (>= 1) kq_matvec_set would
+ * use for this set on the current device, or a negative KQ_ERR_* code if
+ * the set is invalid (the kq_validate_set checks).  Launches nothing.
+ */
+int kq_debug_plan_plane_groups(const kq_tensor* tensors, int32_t n, int32_t ntok);
 
 /* Static description of a status code (never NULL). */
 const char* kq_strerror(int code);

@@ -24,6 +24,7 @@ STATUS = {
 }
 EXPORTS = ("kq_block_bytes", "kq_row_bytes", "kq_matvec", "kq_matvec_set", "kq_matvec_set_noalloc",
            "kq_validate_set", "kq_release_workspace", "kq_debug_set_pipeline", "kq_debug_plan_kernel",
+           "kq_debug_set_plane_groups", "kq_debug_plan_plane_groups",
            "kq_matvec16", "kq_matmul", "kq_embed_rows", "kq_unpack_blocks", "kq_dequant", "kq_debug_read_probe", "kq_strerror",
            "kq_version")
 
@@ -67,6 +68,10 @@ def load() -> ctypes.CDLL:
         L.kq_debug_set_pipeline.restype = ctypes.c_int
         L.kq_debug_plan_kernel.argtypes = [ctypes.POINTER(kq_tensor), i32, i32]
         L.kq_debug_plan_kernel.restype = ctypes.c_int
+        L.kq_debug_set_plane_groups.argtypes = [i32]
+        L.kq_debug_set_plane_groups.restype = ctypes.c_int
+        L.kq_debug_plan_plane_groups.argtypes = [ctypes.POINTER(kq_tensor), i32, i32]
+        L.kq_debug_plan_plane_groups.restype = ctypes.c_int
         L.kq_release_workspace.argtypes = [vp]
         L.kq_release_workspace.restype = ctypes.c_int
         L.kq_unpack_blocks.argtypes = [i32, vp, i64, vp, vp, vp, vp, vp, vp]
@@ -195,9 +200,10 @@ def kq_matvec_set_noalloc(tensors, ntok: int = 1, stream=None, n: int | None = N
     _check(load().kq_matvec_set_noalloc(arr, count, ntok, _stream(stream)), "kq_matvec_set_noalloc")
 
 
-def kq_debug_set_pipeline(on: bool) -> None:
-    """Debug/test: allow (True, the default) or forbid the pipelined kernel."""
-    _check(load().kq_debug_set_pipeline(1 if on else 0), "kq_debug_set_pipeline")
+def kq_debug_set_pipeline(mode) -> None:
+    """Debug/test: which launches may take the pipelined kernel: False or 0
+    none, True or 1 large enough ones (the default), 2 any that fit."""
+    _check(load().kq_debug_set_pipeline(int(mode)), "kq_debug_set_pipeline")
 
 
 def kq_debug_plan_kernel(tensors, ntok: int = 1, n: int | None = None) -> str:
@@ -208,6 +214,22 @@ def kq_debug_plan_kernel(tensors, ntok: int = 1, n: int | None = None) -> str:
     rc = load().kq_debug_plan_kernel(arr, count, ntok)
     _check(rc, "kq_debug_plan_kernel")
     return ("kq_pc_kernel<%d>" if rc == 1 else "kq_matvec_kernel<%d>") % ntok
+
+
+def kq_debug_set_plane_groups(groups: int) -> None:
+    """Debug/test: token-plane groups of the matvec launches: 0 chosen per
+    launch (the default), G >= 1 forced wherever it divides ntok."""
+    _check(load().kq_debug_set_plane_groups(int(groups)), "kq_debug_set_plane_groups")
+
+
+def kq_debug_plan_plane_groups(tensors, ntok: int = 1, n: int | None = None) -> int:
+    """Debug/test: the token-plane groups kq_matvec_set would use for this
+    set on the current device."""
+    arr = tensors if isinstance(tensors, ctypes.Array) else make_set(tensors)
+    count = len(arr) if n is None else n
+    rc = load().kq_debug_plan_plane_groups(arr, count, ntok)
+    _check(rc, "kq_debug_plan_plane_groups")
+    return rc
 
 
 def kq_release_workspace(stream=None) -> None:

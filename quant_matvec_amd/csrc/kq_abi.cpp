@@ -16,7 +16,7 @@ namespace kq {
 int launch_matvec(const KqLaunch& L, hipStream_t stream);
 int launch_capacity(const KqLaunch& L);
 int plan_pipelined(KqLaunch* L);
-void set_pipeline(int on);
+void set_pipeline(int mode);
 int launch_zero(uint32_t* p, int64_t n, hipStream_t stream);
 int scratch_workspace(hipStream_t stream, size_t floats, size_t counters, float** partials, uint32_t** ctrs);
 int launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
@@ -129,31 +129,90 @@ static int validate_tensors(const kq_tensor* t, int32_t n, int32_t ntok, int32_t
 
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok) { return validate_tensors(t, n, ntok, KQ_MAX_NTOK); }
 
-int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L) {
+int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, int32_t groups, KqLaunch* L) {
     *L = KqLaunch{};
-    L->h.n = n;
+    const int32_t planes = ntok / groups;
+    L->h.n = n * groups;
     for (int i = 0; i < kMaxSet; ++i) L->h.wg_end[i] = INT32_MAX;
-    L->ntok = ntok;
+    L->ntok = planes;
     int32_t lds = 0, segs = 0;
     for (int i = 0; i < n; ++i) {
         const kq_tensor& T = t[i];
-        KqDesc& D = L->t[i];
-        D.w = static_cast<const uint8_t*>(T.w);
-        D.x = T.x;
-        D.y = T.y;
-        D.ldx = T.ldx;
-        D.ldy = T.ldy;
-        D.nb = (int32_t)(T.cols / 256);
-        D.row_bytes = (int64_t)D.nb * block_bytes(T.fmt);
-        D.rows = (int32_t)T.rows;
-        D.fmt = T.fmt;
-        plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.nseg, &D.seg, &D.tile_rows);
-        D.tiles = (int32_t)((T.rows + D.tile_rows - 1) / D.tile_rows);
-        segs += D.tiles * D.nseg;
-        if (slot_bytes(T.fmt, ntok, D.tile_rows) > lds) lds = slot_bytes(T.fmt, ntok, D.tile_rows);
+        for (int g = 0; g < groups; ++g) {
+            KqDesc& D = L->t[i * groups + g];
+            D.w = static_cast<const uint8_t*>(T.w);
+            D.x = T.x + (int64_t)g * planes * T.ldx;
+            D.y = T.y + (int64_t)g * planes * T.ldy;
+            D.ldx = T.ldx;
+            D.ldy = T.ldy;
+            D.nb = (int32_t)(T.cols / 256);
+            D.row_bytes = (int64_t)D.nb * block_bytes(T.fmt);
+            D.rows = (int32_t)T.rows;
+            D.fmt = T.fmt;
+            plan_tensor(T.fmt, T.rows, T.cols, ntok, &D.nseg, &D.seg, &D.tile_rows);
+            D.tiles = (int32_t)((T.rows + D.tile_rows - 1) / D.tile_rows);
+            segs += D.tiles * D.nseg;
+            if (slot_bytes(T.fmt, planes, D.tile_rows) > lds) lds = slot_bytes(T.fmt, planes, D.tile_rows);
+        }
     }
     L->total_segments = segs;
     L->lds_bytes = lds;
+    return KQ_OK;
+}
+
+// Token-plane groups.  At ntok >= 3 every tensor runs in 64-row tiles in
+// the one-wave kernel, and a wave's compute grows with ntok while its loads
+// do not: a launch with few segments (the K/V pair: 208 segments at any
+// ntok) leaves most SIMDs idle and waits on a few long waves, and the
+// instances for 3 or more planes read x from LDS without the prefetch that
+// those for 1 and 2 planes have.  Such a launch splits every tensor's planes
+// into G groups of ntok / G, each a member of the same launch planned as at
+// the full ntok, so that G times as many workgroups share the compute; each
+// group re-reads the weights (from the caches at these sizes).  A plane's
+// sums are formed in the same order in every NTOK instance of the kernel,
+// so the bits do not depend on G.  With "fits" meaning that the launch's
+// segments, G times over, fit one round of resident workgroups (and n * G
+// <= kMaxSet), G is
+//   * the smallest divisor of ntok that fits with at most 2 planes a group;
+//   * else the largest divisor that fits;
+//   * else 2 at ntok = 8 for at most kGroupReadBytes of weights (the
+//     8-plane instance is the slowest per plane: a decode set of 16
+//     rotating layers 59 -> 39 us, a Q6_K FFN down 155 -> 86 us, while the
+//     Q4_K FFN matrices lose 3-4% to the second read, and the 202,048-row
+//     LM head, whose second read comes from HBM, 20%);
+//   * else 1.
+// Measured (us per launch, K/V pair at ntok 4 / 6 / 8): 12.7 / 16.7 / 27.4
+// with G = 1, 11.9 / 12.1 / 12.5 as chosen; attention output (832
+// segments) at ntok 4 / 6 / 8: 18.7 / 27.0 / 31.6 -> 17.1 / 19.7 / 21.8.
+constexpr int64_t kGroupReadBytes = (int64_t)128 << 20;
+static int g_plane_groups = 0;       // 0: chosen as above; else forced where it divides ntok
+void set_plane_groups(int g) { g_plane_groups = g < 0 ? 0 : g; }
+
+static int32_t choose_groups(const kq_tensor* t, int32_t n, int32_t ntok) {
+    if (g_plane_groups > 0)
+        return (ntok % g_plane_groups == 0 && n * g_plane_groups <= kMaxSet) ? g_plane_groups : 1;
+    if (ntok < 3) return 1;
+    bool fit[KQ_MAX_NTOK + 1] = {};
+    for (int32_t G = 2; G <= ntok; ++G) {
+        if (ntok % G || n * G > kMaxSet) continue;
+        KqLaunch L;
+        build_launch(t, n, ntok, G, &L);
+        const int cap = launch_capacity(L);
+        fit[G] = cap > 0 && L.total_segments <= cap;
+    }
+    for (int32_t G = 2; G <= ntok; ++G)
+        if (fit[G] && ntok / G <= 2) return G;
+    for (int32_t G = ntok; G >= 2; --G)
+        if (fit[G]) return G;
+    int64_t bytes = 0;
+    for (int i = 0; i < n; ++i) bytes += t[i].rows * (t[i].cols / 256) * block_bytes(t[i].fmt);
+    if (ntok == 8 && n * 2 <= kMaxSet && bytes <= kGroupReadBytes) return 2;
+    return 1;
+}
+
+int plan_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* L) {
+    build_launch(t, n, ntok, choose_groups(t, n, ntok), L);
+    plan_pipelined(L);
     return KQ_OK;
 }
 
@@ -331,8 +390,7 @@ static int release_workspace(hipStream_t stream) {
 // workspace.
 static int enqueue_set(const kq_tensor* tensors, int32_t n, int32_t ntok, hipStream_t s) {
     KqLaunch L;
-    build_launch(tensors, n, ntok, &L);
-    plan_pipelined(&L);
+    plan_launch(tensors, n, ntok, &L);
     const int cap = launch_capacity(L);
     if (cap <= 0) return KQ_ERR_HIP;
     const KqPlanSizes sz = assign_workgroups(&L, cap);
@@ -371,8 +429,8 @@ int kq_matvec_set(const kq_tensor* tensors, int32_t n, int32_t ntok, void* strea
 
 int kq_release_workspace(void* stream) { return release_workspace(static_cast<hipStream_t>(stream)); }
 
-int kq_debug_set_pipeline(int32_t on) {
-    set_pipeline(on);
+int kq_debug_set_pipeline(int32_t mode) {
+    set_pipeline(mode);
     return KQ_OK;
 }
 
@@ -380,9 +438,21 @@ int kq_debug_plan_kernel(const kq_tensor* tensors, int32_t n, int32_t ntok) {
     const int rc = validate_set(tensors, n, ntok);
     if (rc != KQ_OK) return rc;
     KqLaunch L;
-    build_launch(tensors, n, ntok, &L);
-    plan_pipelined(&L);
+    plan_launch(tensors, n, ntok, &L);
     return L.pipelined ? 1 : 0;
+}
+
+int kq_debug_set_plane_groups(int32_t groups) {
+    set_plane_groups(groups);
+    return KQ_OK;
+}
+
+int kq_debug_plan_plane_groups(const kq_tensor* tensors, int32_t n, int32_t ntok) {
+    const int rc = validate_set(tensors, n, ntok);
+    if (rc != KQ_OK) return rc;
+    KqLaunch L;
+    plan_launch(tensors, n, ntok, &L);
+    return ntok / L.ntok;
 }
 
 int kq_matvec_set_noalloc(const kq_tensor* tensors, int32_t n, int32_t ntok, void* stream) {
@@ -390,8 +460,7 @@ int kq_matvec_set_noalloc(const kq_tensor* tensors, int32_t n, int32_t ntok, voi
     if (rc != KQ_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     KqLaunch L;
-    build_launch(tensors, n, ntok, &L);
-    plan_pipelined(&L);
+    plan_launch(tensors, n, ntok, &L);
     const int cap = launch_capacity(L);
     if (cap <= 0) return KQ_ERR_HIP;
     const KqPlanSizes sz = assign_workgroups(&L, cap);

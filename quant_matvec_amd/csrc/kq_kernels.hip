@@ -2154,26 +2154,38 @@ static int capacity_t(int lds_bytes) {
     return min(resident_per_cu<NTOK>(lds_bytes), kMaxWavesPerCU) * cus;
 }
 
-// Whether launches may take the pipelined kernel: on unless the
-// environment sets KQMV_PIPELINE=0, or kq_debug_set_pipeline switched it.
+// Whether launches may take the pipelined kernel: 1 (the default) when
+// they are large enough, 0 never (the environment's KQMV_PIPELINE=0, or
+// kq_debug_set_pipeline), 2 whenever they fit (kq_debug_set_pipeline: tests
+// of small shapes).
 static int g_pipeline = -1;
-void set_pipeline(int on) { g_pipeline = on ? 1 : 0; }
-static bool pipeline_enabled() {
+void set_pipeline(int mode) { g_pipeline = mode < 0 ? 0 : mode > 2 ? 2 : mode; }
+static int pipeline_mode() {
     if (g_pipeline < 0) {
         const char* e = getenv("KQMV_PIPELINE");
         g_pipeline = (e && e[0] == '0') ? 0 : 1;
     }
-    return g_pipeline == 1;
+    return g_pipeline;
 }
 
+// A launch of fewer steps than this many a compute unit takes the one-wave
+// kernel: with a step or two a workgroup the pipeline never fills, and the
+// one-wave kernel's smaller workgroups start sooner (a 256 x 6656 Q4_K
+// matrix 7.6 -> 7.1 us, the 256-row Q6_K + Q5_K pair 9.1 -> 8.7 us; at
+// 6.5 steps a compute unit the two kernels are level).
+constexpr int kPcMinStepsPerCU = 4;
+
 // Sets L up for the pipelined kernel when every tensor runs in 32-row tiles
-// at ntok <= 2 and each tensor's ring of at least 8 step slots, with its 3
-// fold slots, fits one workgroup's LDS: each descriptor gets its ring slots R
-// (even, at most 16) and fold slots TS, the launch its LDS size.  Returns
+// at ntok <= 2, the launch has enough steps (kPcMinStepsPerCU) and each
+// tensor's resident x, its fold slots and a ring of at least every
+// producer's steps in flight fit one workgroup's LDS: each
+// descriptor gets its ring slots R (even, at most 16) and fold slots TS, the
+// launch its LDS size.  Returns
 // whether it did (L->pipelined).
 int plan_pipelined(KqLaunch* L) {
     L->pipelined = 0;
-    if (!pipeline_enabled() || L->ntok > 2) return 0;
+    const int mode = pipeline_mode();
+    if (mode == 0 || L->ntok > 2) return 0;
     static int lds_max[16] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
@@ -2186,6 +2198,7 @@ int plan_pipelined(KqLaunch* L) {
     for (int i = 0; i < L->h.n; ++i) {
         if (L->t[i].tile_rows != 32) return 0;
     }
+    if (mode == 1 && L->total_segments < kPcMinStepsPerCU * compute_units()) return 0;
     for (int i = 0; i < L->h.n; ++i) {
         KqDesc& D = L->t[i];
         int wb = 0, xb = 0, d = 0;

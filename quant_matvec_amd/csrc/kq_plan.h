@@ -57,7 +57,7 @@ struct KqDesc {
     int32_t rows;
     int32_t nb;         // super-blocks per row
     int32_t fmt;
-    int32_t tiles;      // ceil(rows / 64)
+    int32_t tiles;      // ceil(rows / tile_rows)
     int32_t nseg;       // segments per tile row
     int32_t seg;        // S: super-blocks per segment (the last one of a row may be shorter)
     int32_t part_base;  // first shared-tile slot of this tensor in the workspace
@@ -69,7 +69,7 @@ struct KqDesc {
     float* partials;    // this tensor's shared-tile slots in the workspace: [P-1][nseg][ntok][64]
     uint32_t* counters; // this tensor's arrival counters: one per slot, zero between calls
     int32_t tile_rows;  // 64, or 32 for a large matrix (two lanes a row, a segment a step)
-    int32_t reserved0;  // pipelined kernel: weight slots R | fold slots TS << 8 | x slots RX << 16 | steps in flight << 24
+    int32_t reserved0;  // pipelined kernel: weight slots R | fold slots TS << 8
     int64_t reserved1;
 };
 static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
@@ -114,9 +114,16 @@ int32_t slot_bytes(int32_t fmt, int32_t ntok, int32_t tile_rows);
 // Checks (no HIP calls) of a set; KQ_OK or a KQ_ERR_* code.
 int validate_set(const kq_tensor* t, int32_t n, int32_t ntok);
 
-// Fills `out` (workspace pointers and the workgroup split left unset).
-// Assumes validate_set passed.
-int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out);
+// Fills `out` (workspace pointers and the workgroup split left unset) with
+// the tensors' token planes in `groups` groups of ntok / groups planes (a
+// divisor of ntok, n * groups <= kMaxSet): member i * groups + g is plane
+// group g of tensor i, planned as at the full ntok.  Assumes validate_set
+// passed.
+int build_launch(const kq_tensor* t, int32_t n, int32_t ntok, int32_t groups, KqLaunch* out);
+
+// build_launch with the plane groups chosen for the current device (or set
+// by kq_debug_set_plane_groups), then plan_pipelined.
+int plan_launch(const kq_tensor* t, int32_t n, int32_t ntok, KqLaunch* out);
 
 // Splits the launch's workgroups between its tensors for at most
 // `capacity` workgroups: sets wg_base, wg_count, seg_q, seg_r, part_base

@@ -270,10 +270,11 @@ def test_stream52_all_layers_all_rows():
 
 
 # ---- the pipelined producer/consumer kernel against the one-wave kernel:
-# launches whose tensors all run in 32-row tiles at ntok <= 2 take the
-# pipelined kernel; forbidding it makes the same launch run in the one-wave
-# kernel, and both must give the same bits (same plan, same sums in the same
-# order).
+# launches whose tensors all run in 32-row tiles at ntok <= 2 may take the
+# pipelined kernel (by default only with at least four segment steps a
+# compute unit; debug mode 2 at any size); forbidding it makes the same
+# launch run in the one-wave kernel, and both must give the same bits (same
+# plan, same sums in the same order).
 
 PIPE_CASES = [
     ("qkvg set", [(Q4_K, 4096, 6656, 0), (Q6_K, 256, 6656, 0), (Q6_K, 256, 6656, 0), (Q4_K, 4096, 6656, 0)], 1),
@@ -290,6 +291,10 @@ PIPE_CASES = [
 ]
 ONE_WAVE_CASES = ("mixed plans", "long rows", "q6 ntok2")
 PC_CASES = ("qkvg set", "q5 set ntok2", "kv pair small", "ragged large", "one-block segments")
+# of PC_CASES, those with enough steps to take the pipelined kernel by
+# default on a 256-compute-unit GPU (1,768 to 8,151 steps; the others 208
+# and 516)
+DEFAULT_PC_CASES = ("qkvg set", "q5 set ntok2", "ragged large")
 
 
 @pytest.mark.parametrize("name,specs,ntok", PIPE_CASES, ids=[c[0] for c in PIPE_CASES])
@@ -303,26 +308,148 @@ def test_pipelined_kernel_bitwise_equals_one_wave_kernel(name, specs, ntok):
     ws = [kqgen.weights(f, r, c, 681, i, r) for i, (f, r, c, _) in enumerate(specs)]
     dws = [dev(w.reshape(-1)) for w in ws]
     outs = {}
-    for pipe in (True, False):
-        kq.kq_debug_set_pipeline(pipe)
+    for mode in (2, 0):
+        kq.kq_debug_set_pipeline(mode)
         try:
             ys = [t.full((ntok, r), float("nan"), dtype=t.float32, device="cuda") for (_, r, _, _) in specs]
-            note("pipelined vs one-wave: %s ntok=%d pipeline=%s" % (name, ntok, pipe))
+            note("pipelined vs one-wave: %s ntok=%d pipeline mode=%d" % (name, ntok, mode))
             members = kq.make_set([dict(fmt=f, w=dw, x=dxs[xi], y=y, rows=r, cols=c, ldx=xcols[xi])
                                    for (f, r, c, xi), dw, y in zip(specs, dws, ys)])
             kernel = kq.kq_debug_plan_kernel(members, ntok=ntok)
-            if not pipe or name in ONE_WAVE_CASES:
+            if mode == 0 or name in ONE_WAVE_CASES:
                 assert kernel == "kq_matvec_kernel<%d>" % ntok, kernel
             elif name in PC_CASES:
                 assert kernel == "kq_pc_kernel<%d>" % ntok, kernel
             kq.kq_matvec_set(members, ntok=ntok)
-            outs[pipe] = [host(y) for y in ys]
+            outs[mode] = [host(y) for y in ys]
         finally:
-            kq.kq_debug_set_pipeline(True)
+            kq.kq_debug_set_pipeline(1)
+    if t.cuda.get_device_properties(0).multi_processor_count == 256 and name in PC_CASES + ONE_WAVE_CASES:
+        kernel = kq.kq_debug_plan_kernel(members, ntok=ntok)
+        want = "kq_pc_kernel<%d>" if name in DEFAULT_PC_CASES else "kq_matvec_kernel<%d>"
+        assert kernel == want % ntok, (name, kernel)
     for i, ((f, r, c, xi), w) in enumerate(zip(specs, ws)):
-        assert np.array_equal(_bits(outs[True][i]), _bits(outs[False][i])), i
+        assert np.array_equal(_bits(outs[2][i]), _bits(outs[0][i])), i
         x = np.ascontiguousarray(xs[xi][:, :c])
         idx = np.unique(np.concatenate([np.arange(min(r, 70)), np.arange(max(0, r - 70), r),
                                         np.random.default_rng(682).integers(0, r, 300)]))
         y_ref, s = oracle.matvec(f, w, r, c, x, row_idx=idx, nthreads=NTHREADS)
-        check_tol(outs[True][i][:, idx], y_ref, s, "%s member %d" % (name, i))
+        check_tol(outs[2][i][:, idx], y_ref, s, "%s member %d" % (name, i))
+
+
+# ---- the pipelined kernel on small shapes (debug mode 2: it takes any
+# launch that fits, not only those with enough steps): ragged tiles, runs
+# shorter than a tile row, a single step; bitwise against the one-wave
+# kernel and within the bound of the oracle; zero x gives exact zeros and a
+# one-hot x the column of W.
+# (A Q6_K matrix of 6656 columns at two token planes is left out: its x
+# and a full ring do not fit one workgroup's LDS, so it always takes the
+# one-wave kernel.)
+PC_SMALL_SHAPES = [(1, 512), (3, 512), (31, 2560), (33, 6656), (64, 6656), (130, 2560), (257, 6656)]
+PC_SMALL_CASES = [(f, r, c, n) for n in (1, 2) for (r, c) in PC_SMALL_SHAPES for f in FORMATS
+                  if not (f == Q6_K and n == 2 and c == 6656)]
+
+
+@pytest.mark.parametrize("fmt,rows,cols,ntok", PC_SMALL_CASES)
+def test_pipelined_kernel_small_shapes(fmt, rows, cols, ntok):
+    t = torch()
+    w = kqgen.weights(fmt, rows, cols, 690, fmt, rows, cols)
+    dw = dev(w.reshape(-1))
+    W = oracle.dequant(fmt, w, rows, cols)
+    xs = [kqgen.activations(ntok, cols, 691, rows, cols), np.zeros((ntok, cols), np.float32)]
+    # one-hot: token 0 picks the last column (the last block of every row),
+    # token 1 the first
+    hot = [cols - 1, 0][:ntok]
+    onehot = np.zeros((ntok, cols), np.float32)
+    for tk, j in enumerate(hot):
+        onehot[tk, j] = 1.0
+    xs.append(onehot)
+    for k, x in enumerate(xs):
+        dx = dev(x)
+        outs = {}
+        for mode in (2, 0):
+            kq.kq_debug_set_pipeline(mode)
+            try:
+                y = t.full((ntok, rows), float("nan"), dtype=t.float32, device="cuda")
+                note("pipelined small shape fmt=%d %dx%d ntok=%d input %d mode %d" % (fmt, rows, cols, ntok, k, mode))
+                members = kq.make_set([dict(fmt=fmt, w=dw, x=dx, y=y, rows=rows, cols=cols)])
+                want = "kq_pc_kernel<%d>" if mode == 2 else "kq_matvec_kernel<%d>"
+                assert kq.kq_debug_plan_kernel(members, ntok=ntok) == want % ntok
+                kq.kq_matvec_set(members, ntok=ntok)
+                outs[mode] = host(y)
+            finally:
+                kq.kq_debug_set_pipeline(1)
+        assert np.array_equal(_bits(outs[2]), _bits(outs[0])), k
+        if k == 0:
+            y_ref, s = oracle.matvec(fmt, w, rows, cols, x, nthreads=NTHREADS)
+            check_tol(outs[2], y_ref, s, "pipelined small shape")
+        elif k == 1:
+            assert not outs[2].any()
+        else:
+            for tk, j in enumerate(hot):
+                assert np.array_equal(outs[2][tk], W[:, j].astype(np.float32)), tk
+
+
+# ---- token-plane groups: at ntok >= 3 a launch may run each tensor's planes
+# as G groups (members of one launch, planned as at the full ntok); every G
+# must give the bits of G = 1.  The automatic choice: the smallest divisor
+# of ntok with at most 2 planes a group whose segments fit one round of
+# resident workgroups, else the largest divisor that fits, else 2 at ntok 8.
+PLANE_CASES = [
+    ("kv pair", [(Q6_K, 256, 6656, 0), (Q5_K, 256, 6656, 1)]),
+    ("ragged odd blocks", [(Q4_K, 300, 2304, 0), (Q6_K, 77, 768, 1), (Q5_K, 65, 256, 0)]),
+    ("attention output", [(Q4_K, 6656, 4096, 0)]),
+]
+# automatic G on a 256-compute-unit GPU (one-wave capacity 2,048 workgroups):
+# the K/V pair has 208 segments at any ntok, the attention output 832
+AUTO_GROUPS = {("kv pair", 3): 3, ("kv pair", 4): 2, ("kv pair", 6): 3, ("kv pair", 8): 4,
+               ("attention output", 3): 1, ("attention output", 4): 2, ("attention output", 6): 2,
+               ("attention output", 8): 2}
+
+
+@pytest.mark.parametrize("name,specs", PLANE_CASES, ids=[c[0] for c in PLANE_CASES])
+@pytest.mark.parametrize("ntok", [3, 4, 6, 8])
+def test_plane_groups_bitwise(name, specs, ntok):
+    t = torch()
+    xcols = {}
+    for f, r, c, xi in specs:
+        xcols[xi] = max(c, xcols.get(xi, 0))
+    xs = {xi: kqgen.activations(ntok, c, 700, xi, ntok) for xi, c in xcols.items()}
+    dxs = {xi: dev(v) for xi, v in xs.items()}
+    ws = [kqgen.weights(f, r, c, 701, i, r) for i, (f, r, c, _) in enumerate(specs)]
+    dws = [dev(w.reshape(-1)) for w in ws]
+    groups = [g for g in range(1, ntok + 1) if ntok % g == 0 and len(specs) * g <= 16]
+
+    def run(g, noalloc=False):
+        kq.kq_debug_set_plane_groups(g)
+        try:
+            ys = [t.full((ntok, r), float("nan"), dtype=t.float32, device="cuda") for (_, r, _, _) in specs]
+            members = kq.make_set([dict(fmt=f, w=dw, x=dxs[xi], y=y, rows=r, cols=c, ldx=xcols[xi])
+                                   for (f, r, c, xi), dw, y in zip(specs, dws, ys)])
+            want = g if g > 0 else AUTO_GROUPS.get((name, ntok))
+            got = kq.kq_debug_plan_plane_groups(members, ntok=ntok)
+            if want is not None and (g > 0 or t.cuda.get_device_properties(0).multi_processor_count == 256):
+                assert got == want, (g, got, want)
+            note("plane groups: %s ntok=%d G=%d (planned %d)%s" % (name, ntok, g, got, " noalloc" if noalloc else ""))
+            if noalloc:
+                kq.kq_matvec_set_noalloc(members, ntok=ntok)
+            else:
+                kq.kq_matvec_set(members, ntok=ntok)
+            return [host(y) for y in ys]
+        finally:
+            kq.kq_debug_set_plane_groups(0)
+
+    ref = run(1)
+    for g in groups[1:] + [0]:
+        out = run(g)
+        for i in range(len(specs)):
+            assert np.array_equal(_bits(out[i]), _bits(ref[i])), (g, i)
+    out = run(0, noalloc=True)
+    for i in range(len(specs)):
+        assert np.array_equal(_bits(out[i]), _bits(ref[i])), ("noalloc", i)
+    for i, ((f, r, c, xi), w) in enumerate(zip(specs, ws)):
+        x = np.ascontiguousarray(xs[xi][:, :c])
+        idx = np.unique(np.concatenate([np.arange(min(r, 70)), np.arange(max(0, r - 70), r),
+                                        np.random.default_rng(702).integers(0, r, 200)]))
+        y_ref, s = oracle.matvec(f, w, r, c, x, row_idx=idx, nthreads=NTHREADS)
+        check_tol(ref[i][:, idx], y_ref, s, "%s member %d" % (name, i))
