@@ -107,7 +107,26 @@ __device__ __forceinline__ S load_uniform(const S& src) {
 __device__ __forceinline__ uint4 lds_read4(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ uint32_t lds_read1(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
-// Direct global -> LDS loads (the pipelined kernel's producers): every lane
+constexpr int kBufFlags = 0x00020000;           // raw 32-bit buffer resource, no format conversion
+
+// Direct buffer -> LDS loads of the producers' steps: every lane reads SIZE
+// bytes at byte offset off of the buffer r, the wave's 64 pieces land
+// contiguously at lds + SIZE * lane, and a lane whose piece ends past the
+// buffer's size reads nothing from memory (its piece of LDS is filled with
+// zeros), so rows past the tensor's end need no clamp.  The offsets are the
+// lanes' precomputed ones and the base is per step in scalar registers, so a
+// step's addressing costs no vector instruction.  They count in vmcnt until
+// the bytes are in LDS.
+template <int SIZE>
+__device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
+    static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte pieces");
+    if constexpr (SIZE == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+}
+
+// Direct global -> LDS loads (the pipelined kernel's x): every lane
 // reads SIZE bytes at its own address g, and the wave's 64 pieces land
 // contiguously at lds + SIZE * lane (lds is the wave-uniform base).  They
 // count in vmcnt until the bytes are in LDS.
@@ -444,12 +463,16 @@ struct K45Pair {
     // slot, and computes from registers
     static constexpr int LOADS = N;                            // direct loads of one step
     static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
+    // The step's buffer starts at block b of the tile's first row and ends
+    // with block b + 1 of its last row in the tensor.
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
-        const uint32_t max_off = (uint32_t)(rows_here - 1) * (uint32_t)T.row_bytes + 16u * (C2 - 1);
-        gbytes_t col = gbytes(T.w) + (size_t)tile * TR * T.row_bytes + (size_t)b * BB;
+        const int64_t base = (int64_t)tile * TR * T.row_bytes + (int64_t)b * BB;
+        const int size = rows_here * (int)T.row_bytes - b * BB;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(T.w + base), (short)0, size, kBufFlags);
 #pragma unroll
-        for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
+        for (int i = 0; i < N; ++i) kq::dma_buf<16>(r, o.off[i], wslot + 1024 * i);
     }
     struct Regs {
         uint4 v[C];
@@ -819,15 +842,18 @@ struct Q6Pair {
     // the pair's second block
     static constexpr int LOADS = N + 1;                        // direct loads of one step
     static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
+    // The step's buffer starts at the pair's first byte in the tile's first
+    // row (4-byte aligned: b is even) and ends with the pair of its last row
+    // in the tensor.
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
-        const uint32_t rb = (uint32_t)T.row_bytes;
-        const uint32_t max_off = (uint32_t)(rows_here - 1) * rb + 16u * (CH - 1);
-        const uint32_t max104 = (uint32_t)(rows_here - 1) * rb + 416u;
-        gbytes_t col = gbytes(T.w) + (size_t)tile * TR * T.row_bytes + (size_t)210 * b;
+        const int64_t base = (int64_t)tile * TR * T.row_bytes + (int64_t)210 * b;
+        const int size = rows_here * (int)T.row_bytes - 210 * b;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(T.w + base), (short)0, size, kBufFlags);
 #pragma unroll
-        for (int i = 0; i < N; ++i) kq::dma<16>(col + min(o.off[i], max_off), wslot + 1024 * i);
-        kq::dma<4>(col + min(o.off104, max104), wslot + TR * ROWB);
+        for (int i = 0; i < N; ++i) kq::dma_buf<16>(r, o.off[i], wslot + 1024 * i);
+        kq::dma_buf<4>(r, o.off104, wslot + TR * ROWB);
     }
     struct Regs {
         uint32_t wd[53];
@@ -986,7 +1012,6 @@ __device__ __forceinline__ void arrive(const KqDesc& T, int tile, int slot, int 
 // lanes may make go through buffer instructions whose out-of-range offset
 // makes the hardware drop the other lanes.
 constexpr uint32_t kBufDrop = 0x80000000u;      // a buffer offset past every range used here
-constexpr int kBufFlags = 0x00020000;           // raw 32-bit buffer resource, no format conversion
 typedef __attribute__((address_space(3))) volatile uint32_t* lsync_t;
 typedef __attribute__((address_space(3))) uint32_t* lword_t;
 
