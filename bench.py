@@ -94,7 +94,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default="stream52",
-                   choices=["stream52", "qkvg_set", "lm_head", "single_q4k", "kv_pair"])
+                   choices=["stream52", "qkvg_set", "lm_head", "lm_head_q5k", "lm_head_q4k", "single_q4k",
+                            "kv_pair"])
     p.add_argument("--ntok", type=int, default=1, help="kv_pair only")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-other-configs", action="store_true",
@@ -115,6 +116,10 @@ def build_workload(name, ntok):
         return [wl.qkvg_layer(2, i) for i in range(16)], "qkvg_set_x16_rotating", 1
     if name == "lm_head":
         return wl.lm_head(), "lm_head_q6k_202048x6656", 1
+    if name == "lm_head_q5k":
+        return wl.lm_head_q5k(), "lm_head_q5k_202048x6656", 1
+    if name == "lm_head_q4k":
+        return wl.lm_head_q4k(), "lm_head_q4k_202048x6656", 1
     if name == "single_q4k":
         return wl.single_q4k(), "single_q4k_256x6656", 1
     return wl.kv_pair() + wl.kv_pair(swapped=True), "kv_pair_q6k_q5k_ntok%d" % ntok, ntok

@@ -110,6 +110,12 @@ def lm_head_q5k(cfg: int = 7, rows: int = LM_ROWS):
     return [[Tensor("lm_head_q5k", Q5_K, rows, HIDDEN, (cfg, 0, 0), (cfg, 0, 100))]]
 
 
+def lm_head_q4k(cfg: int = 10, rows: int = LM_ROWS):
+    # the same 6656 -> 202,048 shape in Q4_K (the embedding table's format),
+    # for the traffic of the large-matrix path in each format
+    return [[Tensor("lm_head_q4k", Q4_K, rows, HIDDEN, (cfg, 0, 0), (cfg, 0, 100))]]
+
+
 def draft_projections(cfg: int = 8):
     """The draft model's k (Q4_K) and v (Q6_K), 6656 -> 1024 from one x, and
     its fc, 33280 -> 6656 Q4_K."""

@@ -293,6 +293,7 @@ KqPlanSizes assign_workgroups(KqLaunch* L, int32_t capacity) {
         sz.partial_floats += (size_t)ns * D.nseg * L->ntok * kTileRows;
     }
     L->grid = base;
+    L->h.grid = base;
     sz.counters = (size_t)slots;
     return sz;
 }

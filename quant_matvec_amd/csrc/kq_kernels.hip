@@ -1210,12 +1210,13 @@ template <int NTOK>
 __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
     extern __shared__ uint4 kq_slot[];
     uint8_t* slot = reinterpret_cast<uint8_t*>(kq_slot);
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
-    // the head, in one batch of scalar loads
+    // the head, in one batch of scalar loads (it carries the grid size, so
+    // the workgroup's index needs no other kernel-argument load)
     const u32x8* hp = reinterpret_cast<const u32x8*>(&L.h);
     const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2];
     asm volatile("" : : "s"(g0), "s"(g1), "s"(g2));
     const int n = (int)g0[0];
+    const int w = xcd_remap(blockIdx.x, (int)g0[1]);
     // the tensor: count the tensors ending at or before w (the ends are
     // increasing; unused entries are INT32_MAX)
     int i = 0;
@@ -1483,12 +1484,12 @@ __global__ __launch_bounds__(64 * kPcWaves, 1) void kq_pc_kernel(const KqLaunch 
     __shared__ uint32_t kq_pc_sync[PcLayout::words];
     uint8_t* lds = reinterpret_cast<uint8_t*>(kq_pc_lds);
     const lsync_t sync = (lsync_t)(kq_pc_sync);
-    const int w = xcd_remap(blockIdx.x, gridDim.x);
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));    // uniform: scalar bookkeeping
     const u32x8* hp = reinterpret_cast<const u32x8*>(&L.h);
     const u32x8 g0 = hp[0], g1 = hp[1], g2 = hp[2];
     asm volatile("" : : "s"(g0), "s"(g1), "s"(g2));
     const int n = (int)g0[0];
+    const int w = xcd_remap(blockIdx.x, (int)g0[1]);
     int i = 0;
 #pragma unroll
     for (int k = 0; k < kMaxSet; ++k) i += (int)(k < 8 ? g1[k] : g2[k - 8]) <= w ? 1 : 0;

@@ -77,7 +77,8 @@ static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
 // Read by every workgroup before anything else (in one batch).
 struct KqHead {
     int32_t n;
-    int32_t reserved[7];
+    int32_t grid;             // workgroups of the launch (gridDim.x), read with the rest of the head
+    int32_t reserved[6];
     int32_t wg_end[kMaxSet];  // t[i].wg_base + t[i].wg_count; INT32_MAX past the last tensor
 };
 static_assert(sizeof(KqHead) == 96, "head is three 32-byte groups");
