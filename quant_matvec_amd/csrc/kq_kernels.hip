@@ -1723,6 +1723,41 @@ __device__ __forceinline__ void mm16_products(const float (&a)[64], const uint32
     }
 }
 
+// The same with this block's x read from LDS (src: the lane's token row at
+// its group's first element) a quarter at a time, as the products use it:
+// the x of one quarter (16 elements, 16 registers) is live at a time instead
+// of the whole block's, which leaves room for more waves on a SIMD.  The
+// products run in the same order, so the bits are those of mm16_products.
+template <int FMT>
+__device__ __forceinline__ void mm16_products_lds(const float (&a)[64], const uint32_t (&ohdr)[4], const uint8_t* src,
+                                                  float (&acc)[4]) {
+    f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        float xv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = *reinterpret_cast<const float4*>(src + 16 * (4 * k + i));
+            xv[4 * i] = v.x;
+            xv[4 * i + 1] = v.y;
+            xv[4 * i + 2] = v.z;
+            xv[4 * i + 3] = v.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * k + j], xv[j], C, 0, 0, 0);
+        // the next quarter's reads stay after this quarter's products
+        asm volatile("" : "+v"(C) : : "memory");
+    }
+    if constexpr (FMT == KQ_Q6_K) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i]), C[i], acc[i]);
+    } else {
+        (void)ohdr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + C[i];
+    }
+}
+
 template <int FMT>
 __device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
     float a[64];
@@ -1863,13 +1898,8 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
         KQ_MM_LOAD(min(b + 1, nb - 1))
         asm volatile("" : : : "memory");
 #pragma unroll
-        for (int t = 0; t < TT; ++t) {
-            float4 x4[16];
-            const uint8_t* src = xs + (16 * t + r16) * kMmXRow + 256 * g;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) x4[i] = *reinterpret_cast<const float4*>(src + 16 * i);
-            mm16_products<FMT>(a, oh, x4, acc[t]);
-        }
+        for (int t = 0; t < TT; ++t)
+            mm16_products_lds<FMT>(a, oh, xs + (16 * t + r16) * kMmXRow + 256 * g, acc[t]);
     }
 #undef KQ_MM_LOAD
 #pragma unroll
