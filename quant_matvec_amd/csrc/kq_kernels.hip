@@ -1334,9 +1334,18 @@ struct PcLayout {
                          claim = count + kPcMaxFold, xready = claim + 1, sink = xready + 1, words = sink + 64;
 };
 
-// Steps a producer keeps in flight: D * LOADS <= 63 (vmcnt), at most 4.
+// Steps a producer keeps in flight: two (D * LOADS <= 63 for vmcnt).  With
+// fewer requests queued a compute unit, each arrives sooner: against four,
+// the FFN gate + up 37.4 -> 36.2 and 38.6 -> 37.6 us on two boxes, a decode
+// set 15.14 -> 14.87 us on the first and unchanged on the second, the
+// 202,048-row matrices unchanged.
 template <class Col>
-constexpr int pc_depth() { return 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4; }
+constexpr int pc_depth() { return 63 / Col::LOADS < 2 ? 63 / Col::LOADS : 2; }
+
+// The pipelined kernel needs a ring of at least this many step slots: the
+// 19,968-column FFN down, whose resident x leaves room for six Q4_K steps,
+// ran 8% slower in it than in the one-wave kernel (27.1 against 25.0 us).
+constexpr int kPcMinSlots = 8;
 
 // The steps of one producer: positions p, p + kPcProducers, ... of the run.
 // Before issuing position n it waits until position n - R has left its
@@ -2233,8 +2242,8 @@ constexpr int kPcMinStepsPerCU = 4;
 
 // Sets L up for the pipelined kernel when every tensor runs in 32-row tiles
 // at ntok <= 2, the launch has enough steps (kPcMinStepsPerCU) and each
-// tensor's resident x, its fold slots and a ring of at least every
-// producer's steps in flight fit one workgroup's LDS: each
+// tensor's resident x, its fold slots and a ring of at least kPcMinSlots
+// steps fit one workgroup's LDS: each
 // descriptor gets its ring slots R (even, at most 16) and fold slots TS, the
 // launch its LDS size.  Returns
 // whether it did (L->pipelined).
@@ -2263,11 +2272,11 @@ int plan_pipelined(KqLaunch* L) {
         const int TS = min(kPcMaxFold, 2 + (kPcConsumers + D.nseg - 1) / D.nseg);
         const int sums = TS * D.nseg * L->ntok * 128, x_bytes = D.nseg * xb;
         // weight slots: what the rest of the LDS holds (even, at most
-        // kPcMaxSlots), at least every producer's steps in flight, or the
-        // launch takes kq_matvec_kernel
+        // kPcMaxSlots), at least kPcMinSlots (and every producer's steps in
+        // flight), or the launch takes kq_matvec_kernel
         int R = (budget - sums - x_bytes) / wb;
         R = (R > kPcMaxSlots ? kPcMaxSlots : R) & ~1;
-        if (R < kPcProducers * d) return 0;
+        if (R < kPcMinSlots || R < kPcProducers * d) return 0;
         D.reserved0 = R | (TS << 8);
         const int need = R * wb + x_bytes + sums;
         if (need > lds) lds = need;
