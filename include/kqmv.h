@@ -30,9 +30,11 @@
  *     (plane t of x is x + t*ldx; ldx >= cols, ldy >= rows).  x must be
  *     16-byte aligned and ldx a multiple of 4; y must be 4-byte aligned.
  *   - Results are deterministic run to run.  Each output equals the exact
- *     sum of W[i,j]*x[j] within a few float32 rounding steps (the kernels
- *     accumulate in float32 with the per-sub-block scale applied once per
- *     sub-block), so they are not bitwise equal to another kernel's.
+ *     sum of W[i,j]*x[j] within a few float32 rounding steps relative to
+ *     sum_j |W[i,j]*x[j]| (each Q4_K/Q5_K weight is formed with one rounding
+ *     and then multiplied in; Q6_K signed codes are multiplied in and their
+ *     sub-block sum scaled once; sums accumulate in float32 in a fixed
+ *     order), so they are not bitwise equal to another kernel's.
  *   - Up to 16 devices; calls on one device that run concurrently on
  *     different streams are safe.  kq_matvec and kq_matvec_set split long
  *     rows between workgroups; the partial sums of the tiles they share go
@@ -235,8 +237,8 @@ int kq_unpack_blocks(int32_t fmt, const void* w, int64_t nblocks,
 
 /*
  * Debug/test export: dequantized weights as float32 [rows][ldw]
- * (ldw >= cols): Q4_K/Q5_K d*sc_j*q - dmin*m_j, Q6_K d*sc_j*q (muser-book
- * Ch 6 sections 6.2 and 6.4).  Both products are exact in float32 and the
+ * (ldw >= cols): Q4_K/Q5_K d*sc_j*q - dmin*m_j, Q6_K d*sc_j*(q - 32) with q
+ * the unsigned 6-bit code (muser-book Ch 6 sections 6.2 and 6.4).  Both products are exact in float32 and the
  * difference is rounded once, so each value is the exact weight correctly
  * rounded to float32.  The matvec kernels never call this.
  */

@@ -126,19 +126,13 @@ __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
 }
 
-// Direct global -> LDS loads (the pipelined kernel's x): every lane
-// reads SIZE bytes at its own address g, and the wave's 64 pieces land
-// contiguously at lds + SIZE * lane (lds is the wave-uniform base).  They
+// Direct global -> LDS loads of 16 bytes (the pipelined kernel's x): every
+// lane reads 16 bytes at its own address g, and the wave's 64 pieces land
+// contiguously at lds + 16 * lane (lds is the wave-uniform base).  They
 // count in vmcnt until the bytes are in LDS.
-template <int SIZE>
-__device__ __forceinline__ void dma(gbytes_t g, uint8_t* lds) {
-    static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte pieces");
-    if constexpr (SIZE == 16)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
-    else
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                         (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+__device__ __forceinline__ void dma16(gbytes_t g, uint8_t* lds) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 // ------------------------------------------------------------ x staging
@@ -1256,10 +1250,11 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // ------------------------------------------------------------ the pipelined kernel
 // Launches whose tensors all run in 32-row tiles with two-block segments
 // (every decode set and every large matrix at one token plane, at two up to
-// 16384 rows) and whose x fits in LDS beside a full ring take this kernel:
-// one workgroup a compute unit, holding two kinds of waves.
+// 16384 rows), with at least four steps a compute unit, and whose x fits in
+// LDS beside a ring of at least eight steps take this kernel: one workgroup
+// a compute unit, holding two kinds of waves.
 //   * Producers (kPcProducers) only move bytes.  A producer issues the direct
-//     global -> LDS loads of its steps into a ring of LDS slots, keeps several
+//     buffer -> LDS loads of its steps into a ring of LDS slots, keeps two
 //     steps in flight, waits for the oldest with vmcnt and publishes its slot.
 //   * Consumers (kPcConsumers: 12, four waves a SIMD with the producers
 //     within the kernel's 128 registers) only compute.  A free consumer claims the
@@ -1407,7 +1402,7 @@ __device__ __forceinline__ void pc_consume(const KqDesc& T, int j0, int j1, uint
         for (int q = c; q < need * 2 * NTOK; q += kPcConsumers) {
             const int k = q / (2 * NTOK), part = q - k * 2 * NTOK, kb = part / NTOK, t = part - kb * NTOK;
             const int sg = seg0 + k < nseg ? seg0 + k : seg0 + k - nseg;
-            kq::dma<16>(gbytes(T.x) + 4 * (t * T.ldx + 256 * (2 * sg + kb) + 4 * lane),
+            kq::dma16(gbytes(T.x) + 4 * (t * T.ldx + 256 * (2 * sg + kb) + 4 * lane),
                         lds + Y.xs + sg * Y.X + 1024 * part);
         }
         wait_vm<0>();
