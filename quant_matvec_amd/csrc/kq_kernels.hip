@@ -108,22 +108,25 @@ __device__ __forceinline__ uint4 lds_read4(const uint8_t* p) { return *reinterpr
 __device__ __forceinline__ uint32_t lds_read1(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
 constexpr int kBufFlags = 0x00020000;           // raw 32-bit buffer resource, no format conversion
+constexpr int kNonTemporal = 2;                 // cache-policy operand of a load: nt
 
-// Direct buffer -> LDS loads of the producers' steps: every lane reads SIZE
+// Direct buffer -> LDS loads of the producer's steps: every lane reads SIZE
 // bytes at byte offset off of the buffer r, the wave's 64 pieces land
 // contiguously at lds + SIZE * lane, and a lane whose piece ends past the
 // buffer's size reads nothing from memory (its piece of LDS is filled with
 // zeros), so rows past the tensor's end need no clamp.  The offsets are the
 // lanes' precomputed ones and the base is per step in scalar registers, so a
-// step's addressing costs no vector instruction.  They count in vmcnt until
-// the bytes are in LDS.
-template <int SIZE>
+// step's addressing costs no vector instruction.  CP is the loads' cache
+// policy: 0, or kNonTemporal for the weights of a launch of few steps a
+// compute unit (the producer's choice).  They count in vmcnt until the bytes
+// are in LDS.
+template <int SIZE, int CP>
 __device__ __forceinline__ void dma_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* lds) {
     static_assert(SIZE == 16 || SIZE == 4, "16- or 4-byte pieces");
     if constexpr (SIZE == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, CP);
     else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, CP);
 }
 
 // Direct global -> LDS loads of 16 bytes (the pipelined kernel's x): every
@@ -459,6 +462,7 @@ struct K45Pair {
     static constexpr int PC_W = WSLOT, PC_X = 2 * 1024 * NTOK; // LDS bytes of a step's weights, x
     // The step's buffer starts at block b of the tile's first row and ends
     // with block b + 1 of its last row in the tensor.
+    template <int CP>
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
         const int64_t base = (int64_t)tile * TR * T.row_bytes + (int64_t)b * BB;
@@ -466,7 +470,7 @@ struct K45Pair {
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc((void*)(T.w + base), (short)0, size, kBufFlags);
 #pragma unroll
-        for (int i = 0; i < N; ++i) kq::dma_buf<16>(r, o.off[i], wslot + 1024 * i);
+        for (int i = 0; i < N; ++i) kq::dma_buf<16, CP>(r, o.off[i], wslot + 1024 * i);
     }
     struct Regs {
         uint4 v[C];
@@ -839,6 +843,7 @@ struct Q6Pair {
     // The step's buffer starts at the pair's first byte in the tile's first
     // row (4-byte aligned: b is even) and ends with the pair of its last row
     // in the tensor.
+    template <int CP>
     static __device__ __forceinline__ void dma_w(const KqDesc& T, const Offsets& o, int tile, int b, uint8_t* wslot) {
         const int rows_here = min(TR, T.rows - tile * TR);
         const int64_t base = (int64_t)tile * TR * T.row_bytes + (int64_t)210 * b;
@@ -846,8 +851,8 @@ struct Q6Pair {
         const __amdgpu_buffer_rsrc_t r =
             __builtin_amdgcn_make_buffer_rsrc((void*)(T.w + base), (short)0, size, kBufFlags);
 #pragma unroll
-        for (int i = 0; i < N; ++i) kq::dma_buf<16>(r, o.off[i], wslot + 1024 * i);
-        kq::dma_buf<4>(r, o.off104, wslot + TR * ROWB);
+        for (int i = 0; i < N; ++i) kq::dma_buf<16, CP>(r, o.off[i], wslot + 1024 * i);
+        kq::dma_buf<4, CP>(r, o.off104, wslot + TR * ROWB);
     }
     struct Regs {
         uint32_t wd[53];
@@ -1253,11 +1258,12 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // 16384 rows), with at least four steps a compute unit, and whose x fits in
 // LDS beside a ring of at least eight steps take this kernel: one workgroup
 // a compute unit, holding two kinds of waves.
-//   * Producers (kPcProducers) only move bytes.  A producer issues the direct
-//     buffer -> LDS loads of its steps into a ring of LDS slots, keeps two
-//     steps in flight, waits for the oldest with vmcnt and publishes its slot.
-//   * Consumers (kPcConsumers: 12, four waves a SIMD with the producers
-//     within the kernel's 128 registers) only compute.  A free consumer claims the
+//   * The producer (kPcProducers: one wave) only moves bytes.  It issues the
+//     direct buffer -> LDS loads of the run's steps, in order, into a ring of
+//     LDS slots, keeps four steps in flight, waits for the oldest with vmcnt
+//     and publishes its slot.
+//   * Consumers (kPcConsumers: 12; with the producer at most four waves a
+//     SIMD, within the kernel's 128 registers) only compute.  A free consumer claims the
 //     next position of the workgroup's run (an LDS counter), waits for its
 //     slot, copies its lane's block into registers, frees the slot and
 //     computes the step exactly as kq_matvec_kernel does.  Claiming in
@@ -1279,7 +1285,7 @@ __global__ __launch_bounds__(64, 2) void kq_matvec_kernel(const KqLaunch L) {
 // lower positions), so the lowest undelivered position can always go on.
 // Every wait is bounded: a broken handshake ends the wave (wrong results),
 // it never hangs the GPU.
-constexpr int kPcProducers = 2, kPcConsumers = 12, kPcWaves = kPcProducers + kPcConsumers;
+constexpr int kPcProducers = 1, kPcConsumers = 12, kPcWaves = kPcProducers + kPcConsumers;
 constexpr int kPcSpin = 1 << 22;
 
 // s_waitcnt for vmcnt <= N (expcnt and lgkmcnt not waited for)
@@ -1317,9 +1323,11 @@ __device__ __forceinline__ bool spin_until(lsync_t f, uint32_t v) {
 constexpr int kPcMaxSlots = 16, kPcMaxFold = 16;
 struct PcLayout {
     int R, TS, W, X, xs, sums;
+    bool nt;        // non-temporal weight loads
     __device__ __forceinline__ PcLayout(const KqDesc& T, int w, int x) {
         R = T.reserved0 & 255;
         TS = (T.reserved0 >> 8) & 255;
+        nt = (T.reserved0 >> 16) & 1;
         W = w;
         X = x;
         xs = R * W;
@@ -1329,13 +1337,13 @@ struct PcLayout {
                          claim = count + kPcMaxFold, xready = claim + 1, sink = xready + 1, words = sink + 64;
 };
 
-// Steps a producer keeps in flight: two (D * LOADS <= 63 for vmcnt).  With
-// fewer requests queued a compute unit, each arrives sooner: against four,
-// the FFN gate + up 37.4 -> 36.2 and 38.6 -> 37.6 us on two boxes, a decode
-// set 15.14 -> 14.87 us on the first and unchanged on the second, the
-// 202,048-row matrices unchanged.
+// Steps the producer keeps in flight: four (D * LOADS <= 63 for vmcnt).  One
+// producer issuing its steps in order, four deep, against two producers on
+// alternate steps two deep each: a decode set 15.0 -> 14.6 us, 16 rotating
+// sets 14.0 -> 13.5 us, the 202,048-row matrices unchanged (both with
+// non-temporal loads).
 template <class Col>
-constexpr int pc_depth() { return 63 / Col::LOADS < 2 ? 63 / Col::LOADS : 2; }
+constexpr int pc_depth() { return 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4; }
 
 // The pipelined kernel needs a ring of at least this many step slots: the
 // 19,968-column FFN down, whose resident x leaves room for six Q4_K steps,
@@ -1359,7 +1367,8 @@ __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, 
         const int ws = n % Y.R;
         if (n >= Y.R && !spin_until(sync + PcLayout::wdone + ws, (uint32_t)(n - Y.R + 1))) return;
         const int j = j0 + n, tile = j / nseg, b = 2 * (j - tile * nseg);
-        Col::dma_w(T, offs, tile, b, lds + ws * Y.W);
+        if (Y.nt) Col::template dma_w<kNonTemporal>(T, offs, tile, b, lds + ws * Y.W);
+        else Col::template dma_w<0>(T, offs, tile, b, lds + ws * Y.W);
         ++issued;
         // the first step is published once the second is issued (the
         // consumers start sooner), the others with D steps in flight
@@ -2235,6 +2244,15 @@ static int pipeline_mode() {
 // 6.5 steps a compute unit the two kernels are level).
 constexpr int kPcMinStepsPerCU = 4;
 
+// A launch of at most this many steps a compute unit loads its weights with
+// the non-temporal hint.  Measured back to back on one box, against the
+// same kernel with ordinary loads: a decode set (14 steps a compute unit)
+// 14.73 -> 14.43 us, 16 rotating sets 13.92 -> 13.38 us, the attention
+// output (6.5 steps) 10.75 -> 10.56 us, the FFN gate + up (63 steps) 37.8
+// -> 37.4 us; the 202,048-row matrices (320 steps) no faster, and their HBM
+// traffic rose from 1.021 to 1.053 times their bytes.
+constexpr int kPcNtMaxStepsPerCU = 128;
+
 // Sets L up for the pipelined kernel when every tensor runs in 32-row tiles
 // at ntok <= 2, the launch has enough steps (kPcMinStepsPerCU) and each
 // tensor's resident x, its fold slots and a ring of at least kPcMinSlots
@@ -2259,6 +2277,7 @@ int plan_pipelined(KqLaunch* L) {
         if (L->t[i].tile_rows != 32) return 0;
     }
     if (mode == 1 && L->total_segments < kPcMinStepsPerCU * compute_units()) return 0;
+    const int nt = L->total_segments <= kPcNtMaxStepsPerCU * compute_units() ? 1 : 0;
     for (int i = 0; i < L->h.n; ++i) {
         KqDesc& D = L->t[i];
         int wb = 0, xb = 0, d = 0;
@@ -2272,7 +2291,7 @@ int plan_pipelined(KqLaunch* L) {
         int R = (budget - sums - x_bytes) / wb;
         R = (R > kPcMaxSlots ? kPcMaxSlots : R) & ~1;
         if (R < kPcMinSlots || R < kPcProducers * d) return 0;
-        D.reserved0 = R | (TS << 8);
+        D.reserved0 = R | (TS << 8) | (nt << 16);
         const int need = R * wb + x_bytes + sums;
         if (need > lds) lds = need;
     }

@@ -69,7 +69,7 @@ struct KqDesc {
     float* partials;    // this tensor's shared-tile slots in the workspace: [P-1][nseg][ntok][64]
     uint32_t* counters; // this tensor's arrival counters: one per slot, zero between calls
     int32_t tile_rows;  // 64, or 32 for a large matrix (two lanes a row, a segment a step)
-    int32_t reserved0;  // pipelined kernel: weight slots R | fold slots TS << 8
+    int32_t reserved0;  // pipelined kernel: weight slots R | fold slots TS << 8 | non-temporal loads << 16
     int64_t reserved1;
 };
 static_assert(sizeof(KqDesc) == 128, "descriptor is four 32-byte groups");
