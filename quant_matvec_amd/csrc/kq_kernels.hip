@@ -1338,10 +1338,11 @@ struct PcLayout {
 };
 
 // Steps the producer keeps in flight: four (D * LOADS <= 63 for vmcnt).  One
-// producer issuing its steps in order, four deep, against two producers on
-// alternate steps two deep each: a decode set 15.0 -> 14.6 us, 16 rotating
-// sets 14.0 -> 13.5 us, the 202,048-row matrices unchanged (both with
-// non-temporal loads).
+// producer issuing its steps in order, four deep, with non-temporal loads on
+// small launches, against two producers on alternate steps two deep each
+// with ordinary loads: a decode set 15.0 -> 14.6 us, 16 rotating sets 14.0
+// -> 13.5 us, the 202,048-row matrices unchanged.  Two producers gained
+// nothing from the non-temporal hint (a decode set 15.33 us either way).
 template <class Col>
 constexpr int pc_depth() { return 63 / Col::LOADS < 4 ? 63 / Col::LOADS : 4; }
 
