@@ -1371,13 +1371,14 @@ __device__ __forceinline__ void pc_produce(const KqDesc& T, int j0, int nsteps, 
         if (Y.nt) Col::template dma_w<kNonTemporal>(T, offs, tile, b, lds + ws * Y.W);
         else Col::template dma_w<0>(T, offs, tile, b, lds + ws * Y.W);
         ++issued;
-        // the first step is published once the second is issued (the
-        // consumers start sooner), the others with D steps in flight
-        if (published == 0 && issued == 2) {
-            wait_vm<LD>();
-            lds_set(sync + PcLayout::ready + p % Y.R, sync + PcLayout::sink, (uint32_t)(p + 1));
-            ++published;
-        } else if (issued - published == D) {
+        // a step is published with D steps in flight: the first D steps go
+        // out back to back before any wait (publishing the first step as
+        // soon as the second was issued held the third and fourth back until
+        // the first had landed: the 202,048-row Q6_K 197.6 -> 193.0 us, the
+        // FFN gate + up 39.0 -> 37.7 us, the attention output 10.64 ->
+        // 10.12 us, 16 rotating decode sets 13.59 -> 13.28 us; the 52-layer
+        // stream 14.67 -> 14.76 us)
+        if (issued - published == D) {
             wait_vm<(D - 1) * LD>();
             const int pos = p + kPcProducers * published;
             lds_set(sync + PcLayout::ready + pos % Y.R, sync + PcLayout::sink, (uint32_t)(pos + 1));
