@@ -381,16 +381,18 @@ def matvec16_configs(dev):
             out_res["F2_%s_ntok16_%s" % (name, key)] = {
                 "workload": "%s_ntok16" % name, "entry": key, "us_per_tensor": round(us, 3),
                 "weight_GBs": round(wbytes / len(mem) / (us * 1e-6) / 1e9, 1),
-                "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2),
-                "fp32_matrix_peak_frac": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12 / 157.3, 4)}
+                "hbm_frac": round(wbytes / len(mem) / (us * 1e-6) / 8e12, 4),
+                "TFLOPs": round(2 * 16 * weights / len(mem) / (us * 1e-6) / 1e12, 2)}
         del mem
         torch.cuda.empty_cache()
     return out_res
 
 
 def matmul_configs(dev):
-    """A 512-token prefill batch (kq_matmul) through release shapes: fp32
-    matrix-core flops (2 a weight a token) per second."""
+    """A 512-token prefill batch (kq_matmul) through release shapes: flops
+    (2 a weight a token) per second, against the matrix peak of the operand
+    type (Q4_K / Q5_K: bf16, two products a weight and token for x's two
+    parts; Q6_K: float32)."""
     import torch
 
     import kqgen
@@ -418,9 +420,10 @@ def matmul_configs(dev):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         tf = 2 * ntok * T.rows * T.cols / (us * 1e-6) / 1e12
+        matrix, peak = ("bf16", 2500.0 / 2) if T.fmt != 14 else ("f32", 157.3)
         out_res["F4_prefill512_%s" % name] = {"workload": "%s_%dx%d_ntok%d" % (name, T.rows, T.cols, ntok),
                                               "us_per_call": round(us, 1), "TFLOPs": round(tf, 2),
-                                              "fp32_matrix_peak_frac": round(tf / 157.3, 4)}
+                                              "matrix": matrix, "matrix_peak_frac": round(tf / peak, 4)}
         del w, x, y
         torch.cuda.empty_cache()
     return out_res

@@ -1930,6 +1930,218 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
     }
 }
 
+// ------------------------------------------------------------ Q4_K / Q5_K on the bf16 matrix cores
+// The same product for many token planes with v_mfma_f32_16x16x32_bf16 (16
+// times the float32 matrix rate), the operands kept exact enough for the
+// per-row bound (muser-book Ch 6 Figure 6.7 puts prefill on half-precision
+// matrix products; here the half-precision operands are exact):
+// - each sub-block's codes are offset by an integer c = round(dmin*m /
+//   (d*sc)) clamped to the code range, so W = a*(q - c) - b' with a = d*sc,
+//   b' = dmin*m - a*c (one rounding) and |b'| <= |a|/2 where cancellation
+//   can happen; q - c is a small integer, exact in bf16;
+// - x is split into two bf16 parts, hi = bf16(x) and lo = bf16(x - hi), so
+//   hi + lo is x to 2^-18 relative;
+// - per sub-block j and token, C = sum (q - c)*(hi + lo) and X = sum (hi +
+//   lo) come from four products (codes, then all-ones, against each part)
+//   and y += a*C - b'*X.
+// Every error term is then relative to |W_e x_e| (|a*(q - c)| <= 2|W_e| and
+// |b'| <= |W_e| for every element, as the rounding-to-nearest of c gives):
+// the bound is derived in the design notes' tolerance section.
+// Layout: a workgroup of four waves takes four 16-row tiles and 16*TT
+// tokens.  In the products A is x (16 tokens x 32 elements of a sub-block)
+// and B the codes (32 elements x 16 rows): lane l supplies token l % 16 and
+// row l % 16 over elements 8*(l/16) .. +7 of the sub-block, and ends with
+// C for tokens 4*(l/16) + v of its own row l % 16, so the lane's row
+// coefficients scale its own results.  Each block's x (16*TT tokens) is
+// split once by the workgroup into two bf16 planes in LDS.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+constexpr int kMbRow = 528;                  // LDS bytes a token row of one bf16 plane (512 + 16)
+
+// The two bf16 parts of four x values (each pair packed low element first).
+__device__ __forceinline__ void split_x(const float4 v, uint2& hi, uint2& lo) {
+    const bf16x2_t h01 = __builtin_convertvector((f32x2_t){v.x, v.y}, bf16x2_t);
+    const bf16x2_t h23 = __builtin_convertvector((f32x2_t){v.z, v.w}, bf16x2_t);
+    const f32x2_t b01 = __builtin_convertvector(h01, f32x2_t), b23 = __builtin_convertvector(h23, f32x2_t);
+    const bf16x2_t l01 = __builtin_convertvector((f32x2_t){v.x - b01.x, v.y - b01.y}, bf16x2_t);
+    const bf16x2_t l23 = __builtin_convertvector((f32x2_t){v.z - b23.x, v.w - b23.y}, bf16x2_t);
+    hi = make_uint2(__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23));
+    lo = make_uint2(__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23));
+}
+
+// Four codes (bytes of w, each 0..31) minus cf, as bf16 pairs (exact).
+__device__ __forceinline__ uint2 codes_bf16(uint32_t w, float cf) {
+    const f32x2_t a = {(float)(w & 0xFFu) - cf, (float)((w >> 8) & 0xFFu) - cf};
+    const f32x2_t b = {(float)((w >> 16) & 0xFFu) - cf, (float)(w >> 24) - cf};
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_convertvector(a, bf16x2_t)),
+                      __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t)));
+}
+
+template <int FMT, int TT, int KS>
+__global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
+                                                     const float* x, int64_t ldx, int32_t ntok, float* y,
+                                                     int64_t ldy) {
+    static_assert(FMT == KQ_Q4_K || FMT == KQ_Q5_K, "Q4_K and Q5_K");
+    static_assert(KS == 1 || KS == 2 || KS == 4, "1, 2 or 4 waves a tile");
+    constexpr int BB = FMT == KQ_Q4_K ? 144 : 176;
+    constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;      // byte offset of qs
+    constexpr float QMAX = FMT == KQ_Q4_K ? 15.0f : 31.0f;
+    constexpr int kTok = 16 * TT;
+    constexpr int kXP = 4 * TT;                        // float4 pieces of x a thread stages per block
+    constexpr int kXR = kXP * KS;                      // ... per step (KS blocks)
+    constexpr int kPlane = kTok * kMbRow;              // LDS bytes of one block's x, one part
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][KS * kPlane];
+    __shared__ __attribute__((aligned(16))) float xsum[KS][8 * kTok];   // [sub-block][token] sums of x
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, h = lane >> 4;
+    const int ks = wave % KS;                          // this wave's block of each step
+    const int row0 = (blockIdx.x * (4 / KS) + wave / KS) * 16;
+    const int tok0 = blockIdx.y * kTok;
+    const int steps = (nb + KS - 1) / KS;
+    // rows past the matrix repeat its last row; their results are not written
+    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
+    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i <
+    // kXP, of each of the step's KS blocks (tokens past ntok repeat the last
+    // plane, blocks past nb the last block; neither result is used)
+    const float* xcol = x + 4 * (tid & 63);
+    const int xtok = tok0 + (tid >> 6);
+    float acc[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] = 0.0f;
+    u32x4 xr[kXR];
+    uint4 hdr;
+    uint32_t q[8], hb[2];
+    // every step loads the next step's blocks unconditionally (past the
+    // last step it loads the last one again, unused)
+    auto load = [&](int st) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int64_t xb = 256 * (int64_t)min(st * KS + k, nb - 1);
+#pragma unroll
+            for (int i = 0; i < kXP; ++i)
+                xr[k * kXP + i] =
+                    *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + 4 * i, ntok - 1) * ldx + xb);
+        }
+        const int64_t bo = (int64_t)min(st * KS + ks, nb - 1) * BB;
+        hdr = *reinterpret_cast<const uint4*>(arow + bo);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const uint2 v = *reinterpret_cast<const uint2*>(arow + bo + QS + 32 * g + 8 * h);
+            q[2 * g] = v.x;
+            q[2 * g + 1] = v.y;
+        }
+        if constexpr (FMT == KQ_Q5_K) {
+            const uint2 v = *reinterpret_cast<const uint2*>(arow + bo + 16 + 8 * h);
+            hb[0] = v.x;
+            hb[1] = v.y;
+        }
+    };
+    load(0);
+    for (int st = 0; st < steps; ++st) {
+        __syncthreads();                                    // the previous step's LDS reads are done
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int i = 0; i < kXP; ++i) {
+                uint2 hi, lo;
+                const float4 xv = __builtin_bit_cast(float4, xr[k * kXP + i]);
+                split_x(xv, hi, lo);
+                const int off = k * kPlane + ((tid >> 6) + 4 * i) * kMbRow + 8 * (tid & 63);
+                *reinterpret_cast<uint2*>(xs[0] + off) = hi;
+                *reinterpret_cast<uint2*>(xs[1] + off) = lo;
+                // the sub-block's sum of x: four elements here, then over the
+                // eight lanes of the sub-block (lane pairs, quads, half rows)
+                float s4 = (xv.x + xv.y) + (xv.z + xv.w);
+                s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0xB1, 0xF, 0xF, false));
+                s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0x4E, 0xF, 0xF, false));
+                s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0x141, 0xF, 0xF, false));
+                if ((tid & 7) == 0) xsum[k][((tid & 63) >> 3) * kTok + (tid >> 6) + 4 * i] = s4;
+            }
+        const uint4 hd = hdr;
+        uint32_t qq[8], hh[2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) qq[i] = q[i];
+        hh[0] = hb[0];
+        hh[1] = hb[1];
+        __syncthreads();                                    // x of the step's blocks is in LDS
+        load(min(st + 1, steps - 1));
+        asm volatile("" : : : "memory");
+        if (st * KS + ks >= nb) continue;                   // a ragged last step (the wave's own block)
+        const uint8_t* xh_base = xs[0] + ks * kPlane;
+        const uint8_t* xl_base = xs[1] + ks * kPlane;
+        const float d = f16_to_f32(hd.x & 0xFFFFu), dmin = f16_to_f32(hd.x >> 16);
+        const K4Scales S = k4_scales(hd.y, hd.z, hd.w);
+        float blk[TT][4];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) blk[t][v] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int g = j >> 1, sh = 4 * (j & 1);
+            const float a = d * (float)k4_sc(S, j);               // exact
+            const float bm = dmin * (float)k4_m(S, j);            // exact
+            const float cf = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(bm * __builtin_amdgcn_rcpf(a)), 0.0f), QMAX);
+            const float nbp = __builtin_fmaf(a, cf, -bm);         // -(b - a*c), one rounding
+            uint32_t c0 = (qq[2 * g] >> sh) & 0x0F0F0F0Fu, c1 = (qq[2 * g + 1] >> sh) & 0x0F0F0F0Fu;
+            if constexpr (FMT == KQ_Q5_K) {
+                c0 |= ((hh[0] >> j) & 0x01010101u) << 4;
+                c1 |= ((hh[1] >> j) & 0x01010101u) << 4;
+            }
+            const uint2 p0 = codes_bf16(c0, cf), p1 = codes_bf16(c1, cf);
+            const bf16x8_t bq = __builtin_bit_cast(bf16x8_t, make_uint4(p0.x, p0.y, p1.x, p1.y));
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const int off = (16 * t + r16) * kMbRow + 64 * j + 16 * h;
+                const bf16x8_t xh = *reinterpret_cast<const bf16x8_t*>(xh_base + off);
+                const bf16x8_t xl = *reinterpret_cast<const bf16x8_t*>(xl_base + off);
+                const float4 X = *reinterpret_cast<const float4*>(&xsum[ks][j * kTok + 16 * t + 4 * h]);
+                f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+                C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bq, C, 0, 0, 0);
+                C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bq, C, 0, 0, 0);
+                blk[t][0] = __builtin_fmaf(nbp, X.x, __builtin_fmaf(a, C[0], blk[t][0]));
+                blk[t][1] = __builtin_fmaf(nbp, X.y, __builtin_fmaf(a, C[1], blk[t][1]));
+                blk[t][2] = __builtin_fmaf(nbp, X.z, __builtin_fmaf(a, C[2], blk[t][2]));
+                blk[t][3] = __builtin_fmaf(nbp, X.w, __builtin_fmaf(a, C[3], blk[t][3]));
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] += blk[t][v];
+    }
+    if constexpr (KS > 1) {
+        // the tile's KS partial sums, added in wave order by its first wave
+        static_assert(4 * TT * 4 * 64 * 4 <= KS * kPlane, "the partial sums fit in the x plane");
+        float* part = reinterpret_cast<float*>(xs[0]);
+        __syncthreads();                                    // every wave is done with x
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part[((wave * TT + t) * 4 + v) * 64 + lane] = acc[t][v];
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int k = 1; k < KS; ++k) acc[t][v] += part[(((wave + k) * TT + t) * 4 + v) * 64 + lane];
+    }
+    const int row = row0 + r16;
+    if (row < rows) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = tok0 + 16 * t + 4 * h + v;
+                if (tok < ntok) y[(int64_t)tok * ldy + row] = acc[t][v];
+            }
+    }
+}
+
 int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const float* x, int64_t ldx, float* y,
                   int64_t ldy, int32_t ntok, hipStream_t stream) {
     const int32_t nb = (int32_t)(cols / 256);
@@ -1941,11 +2153,11 @@ int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const 
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q4_K, 2, 1>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q5_K, 2, 1>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     default:
@@ -1960,45 +2172,42 @@ int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, cons
                     int64_t ldy, int32_t ntok, hipStream_t stream) {
     const int32_t nb = (int32_t)(cols / 256);
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
-    // split the blocks of a tile over 4 / 2 waves while there are at most
-    // 512 / 1024 tiles (the row count alone decides); beyond that, four row
-    // tiles a workgroup share x through LDS (the same products per output)
     const int64_t tiles = (rows + 15) / 16;
-    const int waves = tiles <= 512 ? 4 : tiles <= 1024 ? 2 : 1;
-    const dim3 grid((unsigned)tiles), block((unsigned)(64 * waves));
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (waves == 1) {
-        const dim3 g4((unsigned)((rows + 63) / 64));
-        switch (fmt) {
-        case KQ_Q4_K:
-            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q4_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
-                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
-            break;
-        case KQ_Q5_K:
-            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q5_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
-                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
-            break;
-        default:
-            hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes,
-                               (int32_t)rows, nb, x, ldx, ntok, y, ldy);
-            break;
+    if (fmt != KQ_Q6_K) {
+        // bf16 matrix products; a tile's blocks split over 4 / 2 waves while
+        // there are at most 512 / 2048 tiles (the row count alone decides;
+        // 4 waves up to 2048 tiles: the FFN gate 59 -> 78 us)
+        const int ks = tiles <= 512 ? 4 : tiles <= 2048 ? 2 : 1;
+        const dim3 g((unsigned)((tiles * ks + 3) / 4));
+#define KQ_MMB16(F, K)                                                                                          \
+    hipLaunchKernelGGL((kq_mmb_kernel<F, 1, K>), g, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x, \
+                       ldx, ntok, y, ldy)
+        if (fmt == KQ_Q4_K) {
+            if (ks == 4) KQ_MMB16(KQ_Q4_K, 4);
+            else if (ks == 2) KQ_MMB16(KQ_Q4_K, 2);
+            else KQ_MMB16(KQ_Q4_K, 1);
+        } else {
+            if (ks == 4) KQ_MMB16(KQ_Q5_K, 4);
+            else if (ks == 2) KQ_MMB16(KQ_Q5_K, 2);
+            else KQ_MMB16(KQ_Q5_K, 1);
         }
+#undef KQ_MMB16
         return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
     }
-    switch (fmt) {
-    case KQ_Q4_K:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q4_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
-        break;
-    case KQ_Q5_K:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q5_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
-        break;
-    default:
-        hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                           ldx, ntok, y, ldy);
-        break;
+    // Q6_K: split the blocks of a tile over 4 / 2 waves while there are at
+    // most 512 / 1024 tiles; beyond that, four row tiles a workgroup share x
+    // through LDS (the same products per output)
+    const int waves = tiles <= 512 ? 4 : tiles <= 1024 ? 2 : 1;
+    const dim3 grid((unsigned)tiles), block((unsigned)(64 * waves));
+    if (waves == 1) {
+        const dim3 g4((unsigned)((rows + 63) / 64));
+        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+                           nb, x, ldx, ntok, y, ldy);
+        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
     }
+    hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
+                       ldx, ntok, y, ldy);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 

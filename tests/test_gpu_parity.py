@@ -502,7 +502,8 @@ def _gpu_matvec16(fmt, w_np, rows, cols, x_np, ldy=None):
 
 @pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("rows,cols,ntok", [(37, 768, 16), (300, 6656, 16), (4100, 2560, 9), (16, 256, 1),
-                                            (1, 512, 16), (16400, 768, 16), (16420, 512, 3)])
+                                            (1, 512, 16), (16400, 768, 16), (16420, 512, 3), (8300, 512, 16),
+                                            (40000, 768, 7)])
 def test_matvec16_parity(fmt, rows, cols, ntok):
     w = kqgen.weights(fmt, rows, cols, 800, fmt, rows, cols)
     x = kqgen.activations(ntok, cols, 801, ntok, cols)
@@ -517,7 +518,7 @@ def test_matvec16_parity(fmt, rows, cols, ntok):
 @pytest.mark.parametrize("fmt", FORMATS)
 def test_matvec16_plane_independent_of_ntok(fmt):
     """A token plane's result is bitwise the same whatever ntok is."""
-    for rows, cols in ((200, 1536), (16420, 512)):     # split tiles; shared-x tiles
+    for rows, cols in ((200, 1536), (8300, 512), (16420, 512), (40000, 768)):   # 4, 2, 2, 1 waves a tile
         w = kqgen.weights(fmt, rows, cols, 802, fmt)
         x = kqgen.activations(16, cols, 803, fmt)
         note("matvec16 planes fmt=%d rows=%d" % (fmt, rows))
