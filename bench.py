@@ -346,7 +346,8 @@ def matvec16_configs(dev):
     stream = torch.cuda.current_stream()
     cases = [("attn_output_q4k_x24", [wl.attn_output(layer=i)[0][0] for i in range(24)], 200),
              ("ffn_gate_q4k_x4", [wl.ffn_gate_up(layer=i)[0][0] for i in range(4)], 50),
-             ("lm_head_q5k", [wl.lm_head_q5k()[0][0]], 10)]
+             ("lm_head_q5k", [wl.lm_head_q5k()[0][0]], 10),
+             ("ffn_down_q6k_x2", [wl.ffn_down(layer=i)[0][0] for i in (1, 3)], 50)]
     for name, tensors, reps in cases:
         print("[bench] generating %s for 16 planes" % name, file=sys.stderr, flush=True)
         mem = []
@@ -390,9 +391,8 @@ def matvec16_configs(dev):
 
 def matmul_configs(dev):
     """A 512-token prefill batch (kq_matmul) through release shapes: flops
-    (2 a weight a token) per second, against the matrix peak of the operand
-    type (Q4_K / Q5_K: bf16, two products a weight and token for x's two
-    parts; Q6_K: float32)."""
+    (2 a weight a token) per second, against the bf16 matrix peak halved
+    (two products a weight and token, one for each of x's two parts)."""
     import torch
 
     import kqgen
@@ -420,7 +420,7 @@ def matmul_configs(dev):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / reps
         tf = 2 * ntok * T.rows * T.cols / (us * 1e-6) / 1e12
-        matrix, peak = ("bf16", 2500.0 / 2) if T.fmt != 14 else ("f32", 157.3)
+        matrix, peak = "bf16", 2500.0 / 2
         out_res["F4_prefill512_%s" % name] = {"workload": "%s_%dx%d_ntok%d" % (name, T.rows, T.cols, ntok),
                                               "us_per_call": round(us, 1), "TFLOPs": round(tf, 2),
                                               "matrix": matrix, "matrix_peak_frac": round(tf / peak, 4)}

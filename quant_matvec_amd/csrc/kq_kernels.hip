@@ -1587,351 +1587,8 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 
-// ------------------------------------------------------------ up to 16 token planes on the matrix cores
-// A weight-stationary tile in the manner of the pages' 16-row verify kernel
-// (Ch 6 section 6.8): a one-wave workgroup owns 16 rows and walks all their
-// blocks once for every token plane.  Per block it issues 64 matrix-core
-// products v_mfma_f32_16x16x4_f32, C[row][token] += A[row][k] * B[k][token]:
-// - lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16], so lane
-//   (r, g) = (l % 16, l / 16) brings row r's elements 64g..64g+63 of the block
-//   and token r's x over the same elements, one element a product;
-// - A is the element's weight and B is x as given (float32).  For Q4_K and
-//   Q5_K the weight is fma(d*sc, q, -dmin*m), the exact value rounded once
-//   (d*sc, dmin*m and (d*sc)*q are exact in float32), so the products sum
-//   W*x directly and nothing is subtracted afterwards.  For Q6_K A is
-//   sc*(q-32), an integer below 2^12 in magnitude (exact), and C is scaled
-//   by the rows' d afterwards: either way every rounding is relative to
-//   |W_e x_e|;
-// - lane l ends with C[4(l/16) + i][l % 16], i < 4: four rows of one token.
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// One block's operands for a lane: the raw bytes of its row's group g and
-// its token's x over the same 64 elements, and the headers of the block in
-// its four output rows.  Loads and use are split so that the next block's
-// loads are in flight while this block's products run.
-template <int FMT, bool WITHX = true>
-struct Mm16Raw {
-    uint4 hdr, q0, q1, h0, h1;        // Q4_K/Q5_K (h0, h1: Q5_K qh)
-    uint32_t ql[17], qh[9], scw[2];   // Q6_K aligned words
-    uint32_t sh;                      // Q6_K: realignment of the block (0 or 16)
-    uint32_t ohdr[4];                 // d|dmin (Q6_K: d) of the output rows
-    float4 xv[16];
-
-    __device__ __forceinline__ void load(const uint8_t* blk, const uint8_t* const (&oblk)[4], const float* xb,
-                                         int g) {
-        if constexpr (FMT == KQ_Q6_K) {
-            // n = g/2: ql[64n..64n+63], qh[32n..32n+31], scales 4g..4g+3, read as
-            // aligned words from the block's 4-byte-aligned base a.  A block
-            // 2 bytes into a word (sh = 16) spans words 0..52 of a, all its
-            // own but the first and last two bytes; a 4-byte-aligned one
-            // (sh = 0) spans words 0..51 and bytes 0-1 of word 52, which end
-            // it.  The words read are a[16n .. 16n+16] (ql, highest 32),
-            // a[32+8n .. 40+8n] (qh, highest 48) and a[48+g], a[48+g+1]
-            // (scales): the last is read only for sh = 16 (word 52 at g = 3,
-            // inside the block); with sh = 0 the alignment ignores it, and
-            // a[48+g] is read again, so nothing past byte 209 of the block
-            // is read.  d of the output rows: the two bytes at 208.
-            const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
-            sh = (reinterpret_cast<uintptr_t>(blk) & 2) ? 16u : 0u;
-            const int n = g >> 1;
-#pragma unroll
-            for (int i = 0; i < 17; ++i) ql[i] = a[16 * n + i];
-#pragma unroll
-            for (int i = 0; i < 9; ++i) qh[i] = a[32 + 8 * n + i];
-            scw[0] = a[48 + g];
-            scw[1] = a[48 + g + (sh >> 4)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ohdr[i] = *reinterpret_cast<const uint16_t*>(oblk[i] + 208);
-        } else {
-            // the lane's own block only: its weights are formed whole in A
-            constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;
-            (void)oblk;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ohdr[i] = 0;
-            hdr = *reinterpret_cast<const uint4*>(blk);
-            q0 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g);
-            q1 = *reinterpret_cast<const uint4*>(blk + QS + 32 * g + 16);
-            if constexpr (FMT == KQ_Q5_K) {
-                h0 = *reinterpret_cast<const uint4*>(blk + 16);
-                h1 = *reinterpret_cast<const uint4*>(blk + 32);
-            }
-        }
-        if constexpr (WITHX) {
-            const float4* xp = reinterpret_cast<const float4*>(xb);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xv[i] = xp[i];
-        }
-    }
-
-    // The A operands of elements 64g..64g+63 in element order: Q6_K
-    // sc*(q-32), Q4_K/Q5_K the weight d*sc*q - dmin*m rounded once.
-    __device__ __forceinline__ void codes(int g, float (&a)[64]) const {
-        if constexpr (FMT == KQ_Q6_K) {
-            // element 64g + j is n = g/2, k = 2(g%2) + j/32, l = j%32 of the layout:
-            // byte j of the ql run (nibble g%2), bits 2k..2k+1 of qh[32n + j%32],
-            // sub-block of 16: 4g + j/16
-            const int nib = 4 * (g & 1);
-            uint32_t L[16], H[8];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) L[i] = __builtin_amdgcn_alignbit(ql[i + 1], ql[i], sh);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) H[i] = __builtin_amdgcn_alignbit(qh[i + 1], qh[i], sh);
-            const uint32_t sc4 = __builtin_amdgcn_alignbit(scw[1], scw[0], sh);
-#pragma unroll
-            for (int j = 0; j < 64; ++j) {
-                const uint32_t lo4 = (L[j >> 2] >> (8 * (j & 3) + nib)) & 15u;
-                const int k = 2 * (g & 1) + (j >> 5);
-                const uint32_t hb = (H[(j & 31) >> 2] >> (8 * (j & 3) + 2 * k)) & 3u;
-                a[j] = (float)(int8_t)(sc4 >> (8 * (j >> 4))) * (float)((int)(lo4 | (hb << 4)) - 32);
-            }
-        } else {
-            const K4Scales S = k4_scales(hdr.y, hdr.z, hdr.w);
-            const float d = f16_to_f32(hdr.x & 0xFFFFu), dmin = f16_to_f32(hdr.x >> 16);
-            const float sl = d * (float)k4_sc(S, 2 * g), shs = d * (float)k4_sc(S, 2 * g + 1);   // exact
-            const float nl = -(dmin * (float)k4_m(S, 2 * g)), nh = -(dmin * (float)k4_m(S, 2 * g + 1));
-            const uint32_t q[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-            const uint32_t h[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    uint32_t lo = (q[i] >> (8 * c)) & 15u, hi = (q[i] >> (8 * c + 4)) & 15u;
-                    if constexpr (FMT == KQ_Q5_K) {
-                        // fifth bit of element e: bit e/32 of qh[e % 32]
-                        lo |= ((h[i] >> (8 * c + 2 * g)) & 1u) << 4;
-                        hi |= ((h[i] >> (8 * c + 2 * g + 1)) & 1u) << 4;
-                    }
-                    a[4 * i + c] = __builtin_fmaf(sl, (float)lo, nl);
-                    a[32 + 4 * i + c] = __builtin_fmaf(shs, (float)hi, nh);
-                }
-            }
-        }
-    }
-};
-
-// acc[i] += one block's contribution to the lane's four outputs, from the
-// block's A operands a (and, for Q6_K, the output rows' d) and one 16-token
-// tile of x
-template <int FMT>
-__device__ __forceinline__ void mm16_products(const float (&a)[64], const uint32_t (&ohdr)[4], const float4 (&x4)[16],
-                                              float (&acc)[4]) {
-    // a lane past ntok carries the last plane's x: its product column is
-    // never written, and a column of C depends only on its own B column
-    float xv[64];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        xv[4 * i] = x4[i].x;
-        xv[4 * i + 1] = x4[i].y;
-        xv[4 * i + 2] = x4[i].z;
-        xv[4 * i + 3] = x4[i].w;
-    }
-    f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int j = 0; j < 64; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], xv[j], C, 0, 0, 0);
-    if constexpr (FMT == KQ_Q6_K) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i]), C[i], acc[i]);
-    } else {
-        (void)ohdr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + C[i];
-    }
-}
-
-// The same with this block's x read from LDS (src: the lane's token row at
-// its group's first element) a quarter at a time, as the products use it:
-// the x of one quarter (16 elements, 16 registers) is live at a time instead
-// of the whole block's, which leaves room for more waves on a SIMD.  The
-// products run in the same order, so the bits are those of mm16_products.
-template <int FMT>
-__device__ __forceinline__ void mm16_products_lds(const float (&a)[64], const uint32_t (&ohdr)[4], const uint8_t* src,
-                                                  float (&acc)[4]) {
-    f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        float xv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 v = *reinterpret_cast<const float4*>(src + 16 * (4 * k + i));
-            xv[4 * i] = v.x;
-            xv[4 * i + 1] = v.y;
-            xv[4 * i + 2] = v.z;
-            xv[4 * i + 3] = v.w;
-        }
-#pragma unroll
-        for (int j = 0; j < 16; ++j) C = __builtin_amdgcn_mfma_f32_16x16x4f32(a[16 * k + j], xv[j], C, 0, 0, 0);
-        // the next quarter's reads stay after this quarter's products
-        asm volatile("" : "+v"(C) : : "memory");
-    }
-    if constexpr (FMT == KQ_Q6_K) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(f16_to_f32(ohdr[i]), C[i], acc[i]);
-    } else {
-        (void)ohdr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = acc[i] + C[i];
-    }
-}
-
-template <int FMT>
-__device__ __forceinline__ void mm16_block(const Mm16Raw<FMT>& r, int g, float (&acc)[4]) {
-    float a[64];
-    r.codes(g, a);
-    mm16_products<FMT>(a, r.ohdr, r.xv, acc);
-}
-
-// A workgroup of `waves` (1, 2 or 4) waves takes one 16-row tile: wave s
-// walks blocks [s*nb/waves, (s+1)*nb/waves) of it, and wave 0 adds the
-// waves' sums in wave order, so a small matrix still fills the GPU.  The
-// split depends on the matrix alone, never on ntok.
-template <int FMT>
-__global__ __launch_bounds__(256) void kq_matvec16_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows,
-                                                           int32_t nb, const float* x, int64_t ldx, int32_t ntok,
-                                                           float* y, int64_t ldy) {
-    constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
-    __shared__ float4 part[4][64];
-    const int waves = (int)(blockDim.x >> 6), s = (int)(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
-    const int row0 = blockIdx.x * 16;
-    const int b0 = (int)((int64_t)s * nb / waves), b1 = (int)((int64_t)(s + 1) * nb / waves);
-    // A rows past the matrix repeat its last row; their results are not written
-    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
-    // a lane past ntok reads the last plane's x (its column is not written)
-    const float* xt = x + (int64_t)min(r16, ntok - 1) * ldx + 64 * g;
-    const uint8_t* orow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
-    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (b0 < b1) {
-        // two operand sets used in turn; every step reloads one
-        // unconditionally (past the last block it reads the last block again,
-        // unused).  The empty asm keeps each set's loads issued where they are
-        // written, ahead of the other set's products, instead of sunk next to
-        // their use.
-        Mm16Raw<FMT> r0, r1;
-        auto load = [&](Mm16Raw<FMT>& r, int b) {
-            b = min(b, b1 - 1);
-            const uint8_t* const ob[4] = {orow[0] + (int64_t)b * BB, orow[1] + (int64_t)b * BB,
-                                          orow[2] + (int64_t)b * BB, orow[3] + (int64_t)b * BB};
-            r.load(arow + (int64_t)b * BB, ob, xt + 256 * (int64_t)b, g);
-        };
-        load(r0, b0);
-        for (int b = b0; b < b1; b += 2) {
-            load(r1, b + 1);
-            asm volatile("" : : : "memory");
-            mm16_block<FMT>(r0, g, acc);
-            if (b + 1 >= b1) break;
-            load(r0, b + 2);
-            asm volatile("" : : : "memory");
-            mm16_block<FMT>(r1, g, acc);
-        }
-    }
-    if (waves > 1) {
-        part[s][lane] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        __syncthreads();
-        if (s != 0) return;
-        float4 v = part[0][lane];
-        for (int k = 1; k < waves; ++k) {
-            const float4 u = part[k][lane];
-            v.x += u.x; v.y += u.y; v.z += u.z; v.w += u.w;
-        }
-        acc[0] = v.x; acc[1] = v.y; acc[2] = v.z; acc[3] = v.w;
-    }
-    if (r16 < ntok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = row0 + 4 * g + i;
-            if (r < rows) y[(int64_t)r16 * ldy + r] = acc[i];
-        }
-    }
-}
-
-// Many token planes (a prefill batch): the same 16-row tile and products.
-// A workgroup of four waves takes four row tiles and 16*TT tokens (TT = 2
-// for a batch; TT = 1 serves the 16-plane call on large matrices), so every
-// block's x (16*TT tokens x 256 floats) is shared by the four waves through
-// LDS: the workgroup loads it once with coalesced 16-byte loads (a token's
-// 1 KB by 64 consecutive lanes), and each wave reads its product operands
-// from LDS for each of its TT 16-token tiles.  Each block's sc*q values
-// are decoded once per wave and used for all TT tiles.  The next block's
-// x and weights are loaded into registers while this block's products run.
-// Token rows in LDS are 1040 bytes apart, so the 16 lanes of a 16-byte LDS
-// read (one per token) fall on distinct banks.  A plane's result does not
-// depend on ntok or on the other planes.
-constexpr int kMmXRow = 1040;              // LDS bytes a token row (1024 + 16)
-
-template <int FMT, int TT>
-__global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
-                                                        const float* x, int64_t ldx, int32_t ntok, float* y,
-                                                        int64_t ldy) {
-    constexpr int BB = FMT == KQ_Q4_K ? 144 : FMT == KQ_Q5_K ? 176 : 210;
-    constexpr int kTok = 16 * TT;          // tokens a workgroup
-    constexpr int kXR = 4 * TT;            // 16-byte x pieces a thread stages per block
-    __shared__ __attribute__((aligned(16))) uint8_t xs[kTok * kMmXRow];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, g = lane >> 4;
-    const int row0 = (blockIdx.x * 4 + wave) * 16;
-    const int tok0 = blockIdx.y * kTok;
-    // rows past the matrix repeat its last row; their results are not written
-    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
-    const uint8_t* orow[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) orow[i] = w + (int64_t)min(row0 + 4 * g + i, rows - 1) * row_bytes;
-    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i < 4*TT
-    // (tokens past ntok repeat the last plane; their columns are not written)
-    const float* xcol = x + 4 * (tid & 63);
-    const int xtok = tok0 + (tid >> 6);
-    float acc[TT][4];
-#pragma unroll
-    for (int t = 0; t < TT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[t][i] = 0.0f;
-    u32x4 xr[kXR];
-    Mm16Raw<FMT, false> r;
-    // every step loads the next block unconditionally (past the last block
-    // it loads the last one again, unused)
-#define KQ_MM_LOAD(b_)                                                                                     \
-    {                                                                                                      \
-        const int64_t bo_ = (int64_t)(b_) * BB;                                                            \
-        _Pragma("unroll") for (int i = 0; i < kXR; ++i)                                                    \
-            xr[i] = *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + 4 * i, ntok - 1) * ldx +     \
-                                                    256 * (int64_t)(b_));                                  \
-        const uint8_t* const ob_[4] = {orow[0] + bo_, orow[1] + bo_, orow[2] + bo_, orow[3] + bo_};        \
-        r.load(arow + bo_, ob_, nullptr, g);                                                               \
-    }
-    KQ_MM_LOAD(0)
-    for (int b = 0; b < nb; ++b) {
-        __syncthreads();                                    // the previous block's LDS reads are done
-#pragma unroll
-        for (int i = 0; i < kXR; ++i)
-            *reinterpret_cast<u32x4*>(xs + ((tid >> 6) + 4 * i) * kMmXRow + 16 * (tid & 63)) = xr[i];
-        float a[64];
-        r.codes(g, a);
-        uint32_t oh[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) oh[i] = r.ohdr[i];
-        __syncthreads();                                    // x of block b is in LDS
-        KQ_MM_LOAD(min(b + 1, nb - 1))
-        asm volatile("" : : : "memory");
-#pragma unroll
-        for (int t = 0; t < TT; ++t)
-            mm16_products_lds<FMT>(a, oh, xs + (16 * t + r16) * kMmXRow + 256 * g, acc[t]);
-    }
-#undef KQ_MM_LOAD
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        const int tok = tok0 + 16 * t + r16;
-        if (tok < ntok) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rr = row0 + 4 * g + i;
-                if (rr < rows) y[(int64_t)tok * ldy + rr] = acc[t][i];
-            }
-        }
-    }
-}
-
-// ------------------------------------------------------------ Q4_K / Q5_K on the bf16 matrix cores
-// The same product for many token planes with v_mfma_f32_16x16x32_bf16 (16
+// ------------------------------------------------------------ many token planes on the bf16 matrix cores
+// Q4_K / Q5_K: the same product for many token planes with v_mfma_f32_16x16x32_bf16 (16
 // times the float32 matrix rate), the operands kept exact enough for the
 // per-row bound (muser-book Ch 6 Figure 6.7 puts prefill on half-precision
 // matrix products; here the half-precision operands are exact):
@@ -1947,16 +1604,19 @@ __global__ __launch_bounds__(256) void kq_matmul_kernel(const uint8_t* w, int64_
 // Every error term is then relative to |W_e x_e| (|a*(q - c)| <= 2|W_e| and
 // |b'| <= |W_e| for every element, as the rounding-to-nearest of c gives):
 // the bound is derived in the design notes' tolerance section.
-// Layout: a workgroup of four waves takes four 16-row tiles and 16*TT
-// tokens.  In the products A is x (16 tokens x 32 elements of a sub-block)
-// and B the codes (32 elements x 16 rows): lane l supplies token l % 16 and
-// row l % 16 over elements 8*(l/16) .. +7 of the sub-block, and ends with
-// C for tokens 4*(l/16) + v of its own row l % 16, so the lane's row
-// coefficients scale its own results.  Each block's x (16*TT tokens) is
-// split once by the workgroup into two bf16 planes in LDS.
+// Layout: a workgroup of NW waves takes NW/KS 16-row tiles and 16*TT
+// tokens, a tile's blocks dealt over KS waves in turn.  In the products A
+// is x (16 tokens x 32 elements of a sub-block) and B the codes (32
+// elements x 16 rows): lane l supplies token l % 16 and row l % 16 over
+// elements 8*(l/16) .. +7 of the sub-block, and ends with C for tokens
+// 4*(l/16) + v of its own row l % 16, so the row's coefficients scale the
+// lane's own results.  Each block's x (16*TT tokens) is split once by the
+// workgroup into two bf16 planes in LDS, with its sub-block sums.
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMbRow = 528;                  // LDS bytes a token row of one bf16 plane (512 + 16)
 
 // The two bf16 parts of four x values (each pair packed low element first).
@@ -1978,29 +1638,30 @@ __device__ __forceinline__ uint2 codes_bf16(uint32_t w, float cf) {
                       __builtin_bit_cast(uint32_t, __builtin_convertvector(b, bf16x2_t)));
 }
 
-template <int FMT, int TT, int KS>
-__global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
+template <int FMT, int TT, int KS, int NW>
+__global__ __launch_bounds__(64 * NW) void kq_mmb_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows, int32_t nb,
                                                      const float* x, int64_t ldx, int32_t ntok, float* y,
                                                      int64_t ldy) {
     static_assert(FMT == KQ_Q4_K || FMT == KQ_Q5_K, "Q4_K and Q5_K");
     static_assert(KS == 1 || KS == 2 || KS == 4, "1, 2 or 4 waves a tile");
+    static_assert(NW == 4 || NW == 8, "four or eight waves a workgroup");
     constexpr int BB = FMT == KQ_Q4_K ? 144 : 176;
     constexpr int QS = FMT == KQ_Q4_K ? 16 : 48;      // byte offset of qs
     constexpr float QMAX = FMT == KQ_Q4_K ? 15.0f : 31.0f;
     constexpr int kTok = 16 * TT;
-    constexpr int kXP = 4 * TT;                        // float4 pieces of x a thread stages per block
+    constexpr int kXP = 16 * TT / NW;                  // float4 pieces of x a thread stages per block
     constexpr int kXR = kXP * KS;                      // ... per step (KS blocks)
     constexpr int kPlane = kTok * kMbRow;              // LDS bytes of one block's x, one part
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][KS * kPlane];
     __shared__ __attribute__((aligned(16))) float xsum[KS][8 * kTok];   // [sub-block][token] sums of x
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, h = lane >> 4;
     const int ks = wave % KS;                          // this wave's block of each step
-    const int row0 = (blockIdx.x * (4 / KS) + wave / KS) * 16;
+    const int row0 = (blockIdx.x * (NW / KS) + wave / KS) * 16;
     const int tok0 = blockIdx.y * kTok;
     const int steps = (nb + KS - 1) / KS;
     // rows past the matrix repeat its last row; their results are not written
     const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
-    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + 4i, i <
+    // staging: thread tid moves float4 tid % 64 of tokens tid/64 + NW*i, i <
     // kXP, of each of the step's KS blocks (tokens past ntok repeat the last
     // plane, blocks past nb the last block; neither result is used)
     const float* xcol = x + 4 * (tid & 63);
@@ -2022,7 +1683,7 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
 #pragma unroll
             for (int i = 0; i < kXP; ++i)
                 xr[k * kXP + i] =
-                    *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + 4 * i, ntok - 1) * ldx + xb);
+                    *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + NW * i, ntok - 1) * ldx + xb);
         }
         const int64_t bo = (int64_t)min(st * KS + ks, nb - 1) * BB;
         hdr = *reinterpret_cast<const uint4*>(arow + bo);
@@ -2048,7 +1709,7 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
                 uint2 hi, lo;
                 const float4 xv = __builtin_bit_cast(float4, xr[k * kXP + i]);
                 split_x(xv, hi, lo);
-                const int off = k * kPlane + ((tid >> 6) + 4 * i) * kMbRow + 8 * (tid & 63);
+                const int off = k * kPlane + ((tid >> 6) + NW * i) * kMbRow + 8 * (tid & 63);
                 *reinterpret_cast<uint2*>(xs[0] + off) = hi;
                 *reinterpret_cast<uint2*>(xs[1] + off) = lo;
                 // the sub-block's sum of x: four elements here, then over the
@@ -2057,7 +1718,7 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
                 s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0xB1, 0xF, 0xF, false));
                 s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0x4E, 0xF, 0xF, false));
                 s4 += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s4), 0x141, 0xF, 0xF, false));
-                if ((tid & 7) == 0) xsum[k][((tid & 63) >> 3) * kTok + (tid >> 6) + 4 * i] = s4;
+                if ((tid & 7) == 0) xsum[k][((tid & 63) >> 3) * kTok + (tid >> 6) + NW * i] = s4;
             }
         const uint4 hd = hdr;
         uint32_t qq[8], hh[2];
@@ -2073,6 +1734,19 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
         const uint8_t* xl_base = xs[1] + ks * kPlane;
         const float d = f16_to_f32(hd.x & 0xFFFFu), dmin = f16_to_f32(hd.x >> 16);
         const K4Scales S = k4_scales(hd.y, hd.z, hd.w);
+        // sub-block coefficients: lane h of a row forms those of sub-blocks
+        // 2h and 2h + 1; the row's other lanes take them by lane permute
+        float ca[2], cc[2], cn[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int sh8 = 8 * (2 * (h & 1) + jj);
+            const uint32_t scw = h < 2 ? S.sc_lo : S.sc_hi, mw = h < 2 ? S.m_lo : S.m_hi;
+            const float a = d * (float)((scw >> sh8) & 0xFFu);            // exact
+            const float bm = dmin * (float)((mw >> sh8) & 0xFFu);         // exact
+            cc[jj] = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(bm * __builtin_amdgcn_rcpf(a)), 0.0f), QMAX);
+            cn[jj] = __builtin_fmaf(a, cc[jj], -bm);                      // -(b - a*c), one rounding
+            ca[jj] = a;
+        }
         float blk[TT][4];
 #pragma unroll
         for (int t = 0; t < TT; ++t)
@@ -2081,10 +1755,10 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int g = j >> 1, sh = 4 * (j & 1);
-            const float a = d * (float)k4_sc(S, j);               // exact
-            const float bm = dmin * (float)k4_m(S, j);            // exact
-            const float cf = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(bm * __builtin_amdgcn_rcpf(a)), 0.0f), QMAX);
-            const float nbp = __builtin_fmaf(a, cf, -bm);         // -(b - a*c), one rounding
+            const int src = 4 * (r16 + 16 * (j >> 1));
+            const float a = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, ca[j & 1])));
+            const float cf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, cc[j & 1])));
+            const float nbp = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, cn[j & 1])));
             uint32_t c0 = (qq[2 * g] >> sh) & 0x0F0F0F0Fu, c1 = (qq[2 * g + 1] >> sh) & 0x0F0F0F0Fu;
             if constexpr (FMT == KQ_Q5_K) {
                 c0 |= ((hh[0] >> j) & 0x01010101u) << 4;
@@ -2114,9 +1788,165 @@ __global__ __launch_bounds__(256) void kq_mmb_kernel(const uint8_t* w, int64_t r
     }
     if constexpr (KS > 1) {
         // the tile's KS partial sums, added in wave order by its first wave
-        static_assert(4 * TT * 4 * 64 * 4 <= KS * kPlane, "the partial sums fit in the x plane");
+        static_assert(NW * TT * 4 * 64 * 4 <= KS * kPlane, "the partial sums fit in the x plane");
         float* part = reinterpret_cast<float*>(xs[0]);
         __syncthreads();                                    // every wave is done with x
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) part[((wave * TT + t) * 4 + v) * 64 + lane] = acc[t][v];
+        __syncthreads();
+        if (ks != 0) return;
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+#pragma unroll
+                for (int k = 1; k < KS; ++k) acc[t][v] += part[(((wave + k) * TT + t) * 4 + v) * 64 + lane];
+    }
+    const int row = row0 + r16;
+    if (row < rows) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int tok = tok0 + 16 * t + 4 * h + v;
+                if (tok < ntok) y[(int64_t)tok * ldy + row] = acc[t][v];
+            }
+    }
+}
+
+// Q6_K on the bf16 matrix cores: W = d*sc_j*(q - 32) over 16-element
+// sub-blocks j, each with its own scale (muser-book Ch 6 Figure 6.5), so
+// each sub-block takes 16x16x16 products: the codes q - 32 (six bits,
+// exact in bf16) against x's two bf16 parts, C_j = sum (q - 32)*(hi + lo),
+// then y += d * sum_j sc_j*C_j (no minimum term, every error relative to
+// |W_e x_e|).  Lane l supplies row l % 16 (and token l % 16) over elements
+// 16j + 4*(l/16) .. +3, whose codes are bytes of one ql word and one qh
+// word of the row's block.
+template <int TT, int KS, int NW>
+__global__ __launch_bounds__(64 * NW) void kq_mmb6_kernel(const uint8_t* w, int64_t row_bytes, int32_t rows,
+                                                          int32_t nb, const float* x, int64_t ldx, int32_t ntok,
+                                                          float* y, int64_t ldy) {
+    static_assert(KS == 1 || KS == 2 || KS == 4, "1, 2 or 4 waves a tile");
+    static_assert(NW == 4 || NW == 8, "four or eight waves a workgroup");
+    constexpr int BB = 210;
+    constexpr int kTok = 16 * TT;
+    constexpr int kXP = 16 * TT / NW;
+    constexpr int kXR = kXP * KS;
+    constexpr int kPlane = kTok * kMbRow;
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][KS * kPlane];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, h = lane >> 4;
+    const int ks = wave % KS;
+    const int row0 = (blockIdx.x * (NW / KS) + wave / KS) * 16;
+    const int tok0 = blockIdx.y * kTok;
+    const int steps = (nb + KS - 1) / KS;
+    const uint8_t* arow = w + (int64_t)min(row0 + r16, rows - 1) * row_bytes;
+    const float* xcol = x + 4 * (tid & 63);
+    const int xtok = tok0 + (tid >> 6);
+    float acc[TT][4];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[t][v] = 0.0f;
+    u32x4 xr[kXR];
+    // the lane's words of the block, read as aligned words from the block's
+    // 4-byte-aligned base a: ql bytes 64n + 32t + 16u + 4h .. +3 (words
+    // 16n + 8t + 4u + h and the next), qh bytes 128 + 32n + 16u + 4h .. +3
+    // (words 32 + 8n + 4u + h and the next), the scales (words 48..51, and
+    // word 52 only when the block starts two bytes into a word), d (the two
+    // bytes at 208).  The highest word read is 48 for ql/qh; word 52 lies
+    // inside a block that starts two bytes into a word, so nothing past
+    // byte 209 of the block is read.
+    uint32_t wq[8][2], wh[4][2], wsc[5], wd, wsh;
+    auto load = [&](int st) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int64_t xb = 256 * (int64_t)min(st * KS + k, nb - 1);
+#pragma unroll
+            for (int i = 0; i < kXP; ++i)
+                xr[k * kXP + i] =
+                    *reinterpret_cast<const u32x4*>(xcol + (int64_t)min(xtok + NW * i, ntok - 1) * ldx + xb);
+        }
+        const uint8_t* blk = arow + (int64_t)min(st * KS + ks, nb - 1) * BB;
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(reinterpret_cast<uintptr_t>(blk) & ~(uintptr_t)3);
+        wsh = (reinterpret_cast<uintptr_t>(blk) & 2) ? 16u : 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {                      // i = 4n + 2t + u
+            wq[i][0] = a[16 * (i >> 2) + 8 * ((i >> 1) & 1) + 4 * (i & 1) + h];
+            wq[i][1] = a[16 * (i >> 2) + 8 * ((i >> 1) & 1) + 4 * (i & 1) + h + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {                      // i = 2n + u
+            wh[i][0] = a[32 + 8 * (i >> 1) + 4 * (i & 1) + h];
+            wh[i][1] = a[32 + 8 * (i >> 1) + 4 * (i & 1) + h + 1];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsc[i] = a[48 + i];
+        wsc[4] = a[51 + (wsh >> 4)];
+        wd = *reinterpret_cast<const uint16_t*>(blk + 208);
+    };
+    load(0);
+    for (int st = 0; st < steps; ++st) {
+        __syncthreads();                                    // the previous step's LDS reads are done
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int i = 0; i < kXP; ++i) {
+                uint2 hi, lo;
+                split_x(__builtin_bit_cast(float4, xr[k * kXP + i]), hi, lo);
+                const int off = k * kPlane + ((tid >> 6) + NW * i) * kMbRow + 8 * (tid & 63);
+                *reinterpret_cast<uint2*>(xs[0] + off) = hi;
+                *reinterpret_cast<uint2*>(xs[1] + off) = lo;
+            }
+        uint32_t ql[8], qh[4], sc[4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ql[i] = __builtin_amdgcn_alignbit(wq[i][1], wq[i][0], wsh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qh[i] = __builtin_amdgcn_alignbit(wh[i][1], wh[i][0], wsh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = __builtin_amdgcn_alignbit(wsc[i + 1], wsc[i], wsh);
+        const float d = f16_to_f32(wd);
+        __syncthreads();                                    // x of the step's blocks is in LDS
+        load(min(st + 1, steps - 1));
+        asm volatile("" : : : "memory");
+        if (st * KS + ks >= nb) continue;                   // a ragged last step (the wave's own block)
+        const uint8_t* xh_base = xs[0] + ks * kPlane;
+        const uint8_t* xl_base = xs[1] + ks * kPlane;
+        float blk[TT][4];
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) blk[t][v] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int n = j >> 3, s = (j >> 1) & 3, u = j & 1;
+            const uint32_t lo4 = (ql[4 * n + 2 * (s & 1) + u] >> (4 * (s >> 1))) & 0x0F0F0F0Fu;
+            const uint32_t hi2 = ((qh[2 * n + u] >> (2 * s)) & 0x03030303u) << 4;
+            const uint2 p = codes_bf16(lo4 | hi2, 32.0f);
+            const short4_t bq = __builtin_bit_cast(short4_t, p);
+            const float scj = (float)((int32_t)(sc[j >> 2] << (24 - 8 * (j & 3))) >> 24);   // exact
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const int off = (16 * t + r16) * kMbRow + 32 * j + 8 * h;
+                const short4_t xh = __builtin_bit_cast(short4_t, *reinterpret_cast<const uint2*>(xh_base + off));
+                const short4_t xl = __builtin_bit_cast(short4_t, *reinterpret_cast<const uint2*>(xl_base + off));
+                f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
+                C = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xh, bq, C, 0, 0, 0);
+                C = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xl, bq, C, 0, 0, 0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) blk[t][v] = __builtin_fmaf(scj, C[v], blk[t][v]);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[t][v] = __builtin_fmaf(d, blk[t][v], acc[t][v]);
+    }
+    if constexpr (KS > 1) {
+        static_assert(NW * TT * 4 * 64 * 4 <= KS * kPlane, "the partial sums fit in the x plane");
+        float* part = reinterpret_cast<float*>(xs[0]);
+        __syncthreads();
 #pragma unroll
         for (int t = 0; t < TT; ++t)
 #pragma unroll
@@ -2148,21 +1978,23 @@ int launch_matmul(int32_t fmt, const void* w, int64_t rows, int64_t cols, const 
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
     // 32 tokens a workgroup: two 16-token tiles (four tiles need more
     // accumulator and staging registers than fit two waves a SIMD, and ran
-    // slower)
+    // slower); Q4_K/Q5_K take eight row tiles a workgroup (four: the
+    // attention output 197 -> 175 us), Q6_K four
     const dim3 grid((unsigned)((rows + 63) / 64), (unsigned)((ntok + 31) / 32));
+    const dim3 grid8((unsigned)((rows + 127) / 128), grid.y);
     const uint8_t* wb = static_cast<const uint8_t*>(w);
     switch (fmt) {
     case KQ_Q4_K:
-        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q4_K, 2, 1>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q4_K, 2, 1, 8>), grid8, dim3(512), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     case KQ_Q5_K:
-        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q5_K, 2, 1>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
+        hipLaunchKernelGGL((kq_mmb_kernel<KQ_Q5_K, 2, 1, 8>), grid8, dim3(512), 0, stream, wb, row_bytes, (int32_t)rows,
                            nb, x, ldx, ntok, y, ldy);
         break;
     default:
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 2>), grid, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
-                           nb, x, ldx, ntok, y, ldy);
+        hipLaunchKernelGGL((kq_mmb6_kernel<2, 1, 8>), grid8, dim3(512), 0, stream, wb, row_bytes, (int32_t)rows, nb,
+                           x, ldx, ntok, y, ldy);
         break;
     }
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
@@ -2174,40 +2006,28 @@ int launch_matvec16(int32_t fmt, const void* w, int64_t rows, int64_t cols, cons
     const int64_t row_bytes = (int64_t)nb * (fmt == KQ_Q4_K ? 144 : fmt == KQ_Q5_K ? 176 : 210);
     const int64_t tiles = (rows + 15) / 16;
     const uint8_t* wb = static_cast<const uint8_t*>(w);
-    if (fmt != KQ_Q6_K) {
-        // bf16 matrix products; a tile's blocks split over 4 / 2 waves while
-        // there are at most 512 / 2048 tiles (the row count alone decides;
-        // 4 waves up to 2048 tiles: the FFN gate 59 -> 78 us)
-        const int ks = tiles <= 512 ? 4 : tiles <= 2048 ? 2 : 1;
-        const dim3 g((unsigned)((tiles * ks + 3) / 4));
-#define KQ_MMB16(F, K)                                                                                          \
-    hipLaunchKernelGGL((kq_mmb_kernel<F, 1, K>), g, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows, nb, x, \
-                       ldx, ntok, y, ldy)
-        if (fmt == KQ_Q4_K) {
-            if (ks == 4) KQ_MMB16(KQ_Q4_K, 4);
-            else if (ks == 2) KQ_MMB16(KQ_Q4_K, 2);
-            else KQ_MMB16(KQ_Q4_K, 1);
-        } else {
-            if (ks == 4) KQ_MMB16(KQ_Q5_K, 4);
-            else if (ks == 2) KQ_MMB16(KQ_Q5_K, 2);
-            else KQ_MMB16(KQ_Q5_K, 1);
-        }
+    // bf16 matrix products, eight waves a workgroup (four: the attention
+    // output 17.1 -> 20.4 us); a tile's blocks split over 4 / 2 waves while
+    // there are at most 512 / 2048 tiles (the row count alone decides; 4
+    // waves up to 2048 tiles: the FFN gate 59 -> 78 us)
+    const int ks = tiles <= 512 ? 4 : tiles <= 2048 ? 2 : 1;
+    const dim3 g((unsigned)((tiles * ks + 7) / 8));
+#define KQ_MMB16(KERNEL)                                                                                         \
+    hipLaunchKernelGGL(KERNEL, g, dim3(512), 0, stream, wb, row_bytes, (int32_t)rows, nb, x, ldx, ntok, y, ldy)
+    if (fmt == KQ_Q4_K) {
+        if (ks == 4) KQ_MMB16((kq_mmb_kernel<KQ_Q4_K, 1, 4, 8>));
+        else if (ks == 2) KQ_MMB16((kq_mmb_kernel<KQ_Q4_K, 1, 2, 8>));
+        else KQ_MMB16((kq_mmb_kernel<KQ_Q4_K, 1, 1, 8>));
+    } else if (fmt == KQ_Q5_K) {
+        if (ks == 4) KQ_MMB16((kq_mmb_kernel<KQ_Q5_K, 1, 4, 8>));
+        else if (ks == 2) KQ_MMB16((kq_mmb_kernel<KQ_Q5_K, 1, 2, 8>));
+        else KQ_MMB16((kq_mmb_kernel<KQ_Q5_K, 1, 1, 8>));
+    } else {
+        if (ks == 4) KQ_MMB16((kq_mmb6_kernel<1, 4, 8>));
+        else if (ks == 2) KQ_MMB16((kq_mmb6_kernel<1, 2, 8>));
+        else KQ_MMB16((kq_mmb6_kernel<1, 1, 8>));
+    }
 #undef KQ_MMB16
-        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
-    }
-    // Q6_K: split the blocks of a tile over 4 / 2 waves while there are at
-    // most 512 / 1024 tiles; beyond that, four row tiles a workgroup share x
-    // through LDS (the same products per output)
-    const int waves = tiles <= 512 ? 4 : tiles <= 1024 ? 2 : 1;
-    const dim3 grid((unsigned)tiles), block((unsigned)(64 * waves));
-    if (waves == 1) {
-        const dim3 g4((unsigned)((rows + 63) / 64));
-        hipLaunchKernelGGL((kq_matmul_kernel<KQ_Q6_K, 1>), g4, dim3(256), 0, stream, wb, row_bytes, (int32_t)rows,
-                           nb, x, ldx, ntok, y, ldy);
-        return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
-    }
-    hipLaunchKernelGGL(kq_matvec16_kernel<KQ_Q6_K>, grid, block, 0, stream, wb, row_bytes, (int32_t)rows, nb, x,
-                       ldx, ntok, y, ldy);
     return hipGetLastError() == hipSuccess ? KQ_OK : KQ_ERR_HIP;
 }
 

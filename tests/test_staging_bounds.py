@@ -128,18 +128,24 @@ def q6_pair(rows, nb):
                 check([(base + o[inside], n)], total, ("Q6Pair dma", rows, nb, tile, b))
 
 
-def mm16_q6_block(o, total):
-    """Mm16Raw::load of the Q6_K block at byte o, every group g: returns the
-    lowest and highest byte read."""
+def mmb6_q6_block(o, total):
+    """kq_mmb6_kernel's loads of the Q6_K block at byte o, every lane group
+    h: returns the lowest and highest byte read."""
     a = o & ~3
     sh = 16 if (o & 2) else 0
     lo, hi = 1 << 62, -1
-    for g in range(4):
-        n = g >> 1
-        words = [16 * n + i for i in range(17)] + [32 + 8 * n + i for i in range(9)] + [48 + g, 48 + g + (sh >> 4)]
+    for h in range(4):
+        words = []
+        for n in range(2):
+            for t in range(2):
+                for u in range(2):
+                    words += [16 * n + 8 * t + 4 * u + h, 16 * n + 8 * t + 4 * u + h + 1]   # ql
+            for u in range(2):
+                words += [32 + 8 * n + 4 * u + h, 32 + 8 * n + 4 * u + h + 1]               # qh
+        words += [48, 49, 50, 51, 51 + (sh >> 4)]                                           # scales
         lo = min(lo, a + 4 * min(words))
         hi = max(hi, a + 4 * max(words) + 3)
-    # d of the output rows: the two bytes at 208
+    # d: the two bytes at 208
     hi = max(hi, o + 209)
     return lo, hi
 
@@ -161,27 +167,30 @@ def test_q6_staging_reads_inside_the_tensor(rows):
 
 def test_q6_matrix_core_loads_stay_in_the_block():
     """Every block of tensors of either block-count parity: nothing past the
-    block's last byte (209), at most the 2 bytes before it."""
+    block's last byte (209), at most the 2 bytes before it (in the same
+    aligned word as the block's first byte)."""
     for rows, nb in ((1, 1), (3, 3), (37, 3), (5, 26), (7, 27)):
         total = rows * nb * 210
         for blk in range(rows * nb):
             o = blk * 210
-            lo, hi = mm16_q6_block(o, total)
+            lo, hi = mmb6_q6_block(o, total)
             assert hi <= o + 209, (rows, nb, blk, hi - o)
             assert lo >= o - 2 and lo >= 0, (rows, nb, blk, lo - o)
             assert hi < total
 
 
 def test_k45_matrix_core_loads_stay_in_the_block():
+    """kq_mmb_kernel's loads of a Q4_K/Q5_K block, every lane group h: the
+    header, two qs words of each group and (Q5_K) two qh words."""
     for fmt in (12, 13):
         bb = BB[fmt]
         qs = 16 if fmt == 12 else 48
-        for g in range(4):
-            pieces = [(0, 16), (qs + 32 * g, 16), (qs + 32 * g + 16, 16)]
+        for h in range(4):
+            pieces = [(0, 16)] + [(qs + 32 * g + 8 * h, 8) for g in range(4)]
             if fmt == 13:
-                pieces += [(16, 16), (32, 16)]
-            for s, n in pieces:
-                assert 0 <= s and s + n <= bb, (fmt, g, s)
+                pieces += [(16 + 8 * h, 8)]
+            for st, n in pieces:
+                assert 0 <= st and st + n <= bb, (fmt, h, st)
 
 
 def test_the_model_catches_a_read_past_the_end():
