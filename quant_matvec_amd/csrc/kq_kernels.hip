@@ -1598,12 +1598,13 @@ int launch_embed(const uint8_t* table, int64_t rows, int64_t cols, const int32_t
 //   can happen; q - c is a small integer, exact in bf16;
 // - x is split into two bf16 parts, hi = bf16(x) and lo = bf16(x - hi), so
 //   hi + lo is x to 2^-18 relative;
-// - per sub-block j and token, C = sum (q - c)*(hi + lo) and X = sum (hi +
-//   lo) come from four products (codes, then all-ones, against each part)
-//   and y += a*C - b'*X.
+// - per sub-block j and token, C_j = sum (q - c)*(hi + lo) comes from two
+//   bf16 products (codes against each part); X_j, the sub-block's sum of x,
+//   is summed in float32 when x is staged;
+// - a block adds sum_j a_j*C_j - sum_j b'_j*X_j into the row, the second
+//   sum over the eight sub-blocks as two float32 products.
 // Every error term is then relative to |W_e x_e| (|a*(q - c)| <= 2|W_e| and
-// |b'| <= |W_e| for every element, as the rounding-to-nearest of c gives):
-// the bound is derived in the design notes' tolerance section.
+// |b'| <= |W_e| for every element, as the rounding-to-nearest of c gives).
 // Layout: a workgroup of NW waves takes NW/KS 16-row tiles and 16*TT
 // tokens, a tile's blocks dealt over KS waves in turn.  In the products A
 // is x (16 tokens x 32 elements of a sub-block) and B the codes (32
@@ -1747,18 +1748,25 @@ __global__ __launch_bounds__(64 * NW) void kq_mmb_kernel(const uint8_t* w, int64
             cn[jj] = __builtin_fmaf(a, cc[jj], -bm);                      // -(b - a*c), one rounding
             ca[jj] = a;
         }
+        // the offset terms sum_j -b'_j * X_j of the block, for every row and
+        // token of the tile, as two float32 products over the sub-blocks:
+        // lane group h brings sub-blocks 2h (first) and 2h + 1 (second),
+        // whose -b' it formed itself
         float blk[TT][4];
 #pragma unroll
-        for (int t = 0; t < TT; ++t)
+        for (int t = 0; t < TT; ++t) {
+            f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+            O = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[ks][(2 * h) * kTok + 16 * t + r16], cn[0], O, 0, 0, 0);
+            O = __builtin_amdgcn_mfma_f32_16x16x4f32(xsum[ks][(2 * h + 1) * kTok + 16 * t + r16], cn[1], O, 0, 0, 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) blk[t][v] = 0.0f;
+            for (int v = 0; v < 4; ++v) blk[t][v] = O[v];
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int g = j >> 1, sh = 4 * (j & 1);
             const int src = 4 * (r16 + 16 * (j >> 1));
             const float a = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, ca[j & 1])));
             const float cf = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, cc[j & 1])));
-            const float nbp = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src, __builtin_bit_cast(int, cn[j & 1])));
             uint32_t c0 = (qq[2 * g] >> sh) & 0x0F0F0F0Fu, c1 = (qq[2 * g + 1] >> sh) & 0x0F0F0F0Fu;
             if constexpr (FMT == KQ_Q5_K) {
                 c0 |= ((hh[0] >> j) & 0x01010101u) << 4;
@@ -1771,14 +1779,11 @@ __global__ __launch_bounds__(64 * NW) void kq_mmb_kernel(const uint8_t* w, int64
                 const int off = (16 * t + r16) * kMbRow + 64 * j + 16 * h;
                 const bf16x8_t xh = *reinterpret_cast<const bf16x8_t*>(xh_base + off);
                 const bf16x8_t xl = *reinterpret_cast<const bf16x8_t*>(xl_base + off);
-                const float4 X = *reinterpret_cast<const float4*>(&xsum[ks][j * kTok + 16 * t + 4 * h]);
                 f32x4 C = {0.0f, 0.0f, 0.0f, 0.0f};
                 C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xh, bq, C, 0, 0, 0);
                 C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xl, bq, C, 0, 0, 0);
-                blk[t][0] = __builtin_fmaf(nbp, X.x, __builtin_fmaf(a, C[0], blk[t][0]));
-                blk[t][1] = __builtin_fmaf(nbp, X.y, __builtin_fmaf(a, C[1], blk[t][1]));
-                blk[t][2] = __builtin_fmaf(nbp, X.z, __builtin_fmaf(a, C[2], blk[t][2]));
-                blk[t][3] = __builtin_fmaf(nbp, X.w, __builtin_fmaf(a, C[3], blk[t][3]));
+#pragma unroll
+                for (int v = 0; v < 4; ++v) blk[t][v] = __builtin_fmaf(a, C[v], blk[t][v]);
             }
         }
 #pragma unroll
